@@ -1,0 +1,186 @@
+"""Throughput of steady wavefront rounds on one MI355X.
+
+A step is one whole round (for every layer: K/V publish, then the batched
+wavefront attention; then commit) of the Wan2.1-1.3B-shaped 4-step request:
+S = 4, W = 4 (store window 8), 4680 tokens per chunk, 12 heads x 128, 30
+layers, bf16.  Rounds 0..12 fill the pipeline and the history window
+(untimed); warmup rounds follow; then exactly `--steps` steady rounds are
+timed between two device synchronisations.  Inputs (two seeded sets,
+alternating by round) are resident in HBM before timing starts.
+
+Output: one JSON line.  `value` = rounds per second (one chunk completes per
+round).  `roofline` is the attention kernel's: algorithmic FLOPs per launch
+(readable key tokens only) / its mean duration from HIP events recorded on
+the launch stream around every attention launch in the timed region.
+`cpu_baseline` is the fp64 oracle on a bounded sample, timed on this host.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="wan1.3b_4step")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=1,
+                    help="heads of one layer the oracle baseline times")
+    return ap.parse_args()
+
+
+def oracle_baseline(w, k, layer, heads, raw):
+    """Time the oracle on `heads` of one layer of round k (every group)."""
+    import numpy as np  # noqa: F401
+    from oracle import wf_plan as P
+    from oracle import wf_round as WR
+
+    oc = P.Config(S=w.S, W=w.W, W_store=w.W_store, anchor=w.anchor, n_chunk=w.n_chunk, F=w.F,
+                  Hh=w.Hh, Ww=w.Ww, n_heads=w.n_heads, head_dim=w.head_dim,
+                  n_layers=w.n_layers, mask=w.mask)
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 0) for i in threadpool_info()), default=None)
+    except Exception:
+        pass
+    t0 = time.perf_counter()
+    for s in range(w.S + 1):
+        if P.chunk_active(oc, k - s):
+            WR.group_output(oc, k, s, layer, raw, heads=heads)
+    dt = time.perf_counter() - t0
+    frac = len(heads) / (w.n_heads * w.n_layers)   # share of one round
+    t_round = dt / frac
+    cores = len(os.sched_getaffinity(0))
+    return {"value": 1.0 / t_round, "unit": "rounds/s", "cores": threads or cores,
+            "kind": "oracle",
+            "sample": f"fp64 oracle, round k={k}, layer {layer}, heads {list(heads)} of "
+                      f"{w.n_heads}, every query group over its full context: {dt:.1f} s, "
+                      f"scaled by {1 / frac:.0f} to one round ({w.n_layers} layers x "
+                      f"{w.n_heads} heads); host has {cores} cores"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the round's multi-GPU sharding is described, not built)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from chunk_causal_dit_round_amd import synth, wf
+    from chunk_causal_dit_round_amd.session import Session
+    from chunk_causal_dit_round_amd.workloads import ALL
+
+    w = ALL[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sess = Session(w.config(), device=dev)
+    S, L = w.S, w.n_layers
+    w_store = w.W + w.S if w.W_store < 0 else w.W_store
+    k_steady = w.S + max(w.W, w_store) + 1         # full width and full window
+    n_rounds = w.n_chunk + w.S
+    if k_steady + args.warmup + args.steps > w.n_chunk:
+        print("steps + warmup exceed the steady rounds of one request", file=sys.stderr)
+        sys.exit(2)
+
+    # Two resident input sets; round r uses set r % 2.
+    sets = [sess.bufs, sess.alloc_io()]
+    for i, b in enumerate(sets):
+        synth.fill_round(b, "bench", i, L, S + 1)
+        if i == 1:
+            b["q_rot"], b["out"] = sets[0]["q_rot"], sets[0]["out"]
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def run_round(k, ev=None):
+        b = sets[k % 2]
+        plan = sess.plan(k)
+        if ev is None:
+            sess.run_round(plan, b, stream)
+            return plan
+        for layer in range(L):
+            ev[0][layer].record(stream)
+            sess.publish(plan, layer, b, stream)
+            ev[1][layer].record(stream)
+            sess.attention(plan, layer, b, stream)
+            ev[2][layer].record(stream)
+        sess.commit(plan)
+        return plan
+
+    for k in range(k_steady + args.warmup):
+        run_round(k)
+    torch.cuda.synchronize()
+
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(L)] for _ in range(3)]
+              for _ in range(args.steps)]
+    k0 = k_steady + args.warmup
+    plans = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        plans.append(run_round(k0 + i, events[i]))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    elapsed = t1 - t0
+    ms_step = 1e3 * elapsed / args.steps
+    att_ms = [e[1][l].elapsed_time(e[2][l]) for e in events for l in range(L)]
+    pub_ms = [e[0][l].elapsed_time(e[1][l]) for e in events for l in range(L)]
+    att_avg = sum(att_ms) / len(att_ms)
+    pub_avg = sum(pub_ms) / len(pub_ms)
+    flops_launch = plans[0].flops / L            # every timed round is steady: same work
+    pub_bytes_launch = plans[0].publish_bytes / L
+    achieved = flops_launch / (att_avg * 1e-3) / 1e12
+    total_flops = sum(p.flops for p in plans)
+
+    res = {
+        "metric": "wavefront rounds/sec (=chunks/sec) and attention TFLOP/s vs bf16 MFMA peak",
+        "value": args.steps / elapsed,
+        "unit": "rounds/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name} steady wavefront round", "S": w.S, "W": w.W,
+                   "W_store": w_store, "anchor": w.anchor, "n_chunk": w.n_chunk,
+                   "tokens_per_chunk": w.n_tokens, "heads": w.n_heads,
+                   "head_dim": w.head_dim, "layers": L,
+                   "rounds_timed": [k0, k0 + args.steps - 1], "n_rounds": n_rounds},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "kernel": "wf_attention_bf16_kernel<128>",
+                     "flops_per_launch": flops_launch, "avg_launch_ms": att_avg},
+        "attention_tflops_round": total_flops / elapsed / 1e12,
+        "publish": {"avg_launch_ms": pub_avg, "bytes_per_launch": pub_bytes_launch,
+                    "gbps": pub_bytes_launch / (pub_avg * 1e-3) / 1e9,
+                    "hbm_frac": pub_bytes_launch / (pub_avg * 1e-3) / 1e9 / PEAK_HBM_GBPS},
+    }
+
+    if not args.no_cpu_baseline:
+        def raw(rnd, layer, stage, name):
+            x = synth.slice_input("bench", rnd % 2, layer, stage, name, sess.N, sess.H, sess.D,
+                                  dev, sess.dtype)
+            return x.to(torch.float64).cpu().numpy()
+        res["cpu_baseline"] = oracle_baseline(w, k0, 0, list(range(args.cpu_heads)), raw)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,81 @@
+"""Builds ``libwf.so`` (HIP kernels + C ABI) in-tree for gfx950.
+
+Usage: ``python -m chunk_causal_dit_round_amd.build`` or ``build_library()``.
+Always recompiles.  A host-only variant of the scheduler (``g++`` with
+sanitizers) is built by ``build_host_check()`` for CPU tests.
+"""
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libwf.so")
+ARCH = "gfx950"
+
+HIP_SOURCES = ["wf_runtime.cpp", "wf_publish.hip", "wf_attention.hip"]
+CXX_SOURCES = ["wf_plan.cpp"]
+
+# Packed fp32 VALU forms are switched off for all device code.
+HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-Wall", "-Wno-unused-command-line-argument"]
+
+
+def _hipcc():
+    for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"build failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    if verbose and r.stderr.strip():
+        print(r.stderr, file=sys.stderr)
+
+
+def build_library(verbose: bool = False) -> str:
+    """Compile every source and link ``libwf.so``; returns its path."""
+    os.makedirs(BUILD, exist_ok=True)
+    hipcc = _hipcc()
+    objs = []
+    for src in CXX_SOURCES:
+        obj = os.path.join(BUILD, src + ".o")
+        _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC,
+              "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        objs.append(obj)
+    for src in HIP_SOURCES:
+        obj = os.path.join(BUILD, src + ".o")
+        lang = ["-x", "hip"] if src.endswith(".cpp") else []
+        _run([hipcc, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, *lang,
+              "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        objs.append(obj)
+    tmp = LIB + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def build_host_check(verbose: bool = False) -> str:
+    """Host-only scheduler + checker built with ASan/UBSan (no HIP)."""
+    os.makedirs(BUILD, exist_ok=True)
+    exe = os.path.join(BUILD, "plan_check")
+    _run(["g++", "-O1", "-g", "-std=c++17", "-fsanitize=address,undefined",
+          "-fno-sanitize-recover=all", "-Wall", "-I", INCLUDE, "-I", CSRC,
+          os.path.join(CSRC, "wf_plan.cpp"), os.path.join(CSRC, "plan_check.cpp"),
+          "-o", exe], verbose)
+    return exe
+
+
+if __name__ == "__main__":
+    print(build_library(verbose=True))

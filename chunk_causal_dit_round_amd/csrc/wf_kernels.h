@@ -1,0 +1,73 @@
+// Kernel argument blocks and launchers shared by the host runtime and the
+// HIP kernels.  Arguments travel by value in the kernarg segment; nothing is
+// staged through device memory.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "wf.h"
+
+namespace wf {
+
+// ------------------------------------------------------------ publish ----
+enum : int32_t {
+  TASK_CELL = 0,     // rotate q and k of one cell, write q_rot and its page
+  TASK_CAPTURE = 1,  // TASK_CELL that also keeps the raw k and v^T (anchor)
+  TASK_ANCHOR = 2    // re-rotate the kept anchor key into the anchor slot
+};
+
+struct PublishTask {
+  int32_t stage;   // input stage (cell) the rows come from; unused for anchor
+  int32_t slot;    // destination slot in this layer's pool
+  int32_t frame0;  // frame position of the chunk's first frame
+  int32_t mode;    // TASK_*
+};
+
+struct PublishArgs {
+  const void* q;          // this layer's [S+1][N][H][D]
+  const void* k;
+  const void* v;
+  void* q_rot;            // this layer's [S+1][N][H][D]
+  void* pool;             // this layer's [n_slots] pages
+  void* anchor_raw;       // this layer's anchor page (raw K, Vt)
+  const float2* rope;     // [n_frames*nt | Hh*nh | Ww*nw] (cos, sin)
+  int64_t page_elems;     // 2 H N D
+  int32_t N, H, D, F, Hh, Ww;
+  int32_t nt, nh, nw, n_frames;
+  int32_t n_tasks;
+  int32_t pad_;
+  PublishTask task[WF_MAX_GROUPS + 1];
+};
+
+// ---------------------------------------------------------- attention ----
+struct AttnGroup {
+  int32_t stage;     // query rows come from q_rot[stage]
+  int32_t n_pages;   // key pages in context order
+  int32_t item0;     // first work item of this group
+  uint16_t slot[WF_MAX_PAGES];
+};
+
+struct AttnArgs {
+  const void* q_rot;   // [S+1][N][H][D]
+  void* out;           // [S+1][N][H][D]
+  const void* pool;    // this layer's [n_slots] pages
+  int64_t page_elems;
+  int32_t N, H, D;
+  float scale_log2e;   // softmax scale * log2(e)
+  int32_t n_groups;    // active groups, longest context first
+  int32_t q_tiles;     // query tiles per (group, head)
+  int32_t n_items;     // sum over groups of H * q_tiles
+  int32_t pad_;
+  AttnGroup grp[WF_MAX_GROUPS];
+};
+
+// Query rows per work item of each attention instance.
+constexpr int kAttnBM_bf16 = 128;
+constexpr int kAttnBM_f32 = 64;
+
+hipError_t launch_publish(const PublishArgs& a, int dtype, hipStream_t stream);
+hipError_t launch_attention(const AttnArgs& a, int dtype, hipStream_t stream);
+
+}  // namespace wf

@@ -1,0 +1,190 @@
+// Round scheduler and page allocator (see wf_plan.h for the sources).
+#include "wf_plan.h"
+
+#include <cmath>
+#include <cstring>
+
+namespace wf {
+namespace {
+
+bool mul_ok(size_t a, size_t b, size_t* r) { return !__builtin_mul_overflow(a, b, r); }
+
+bool fail(std::string* why, const char* msg) {
+  if (why) *why = msg;
+  return false;
+}
+
+// Chunk i exists in the request.
+inline bool live(const Shape& sh, int64_t i) { return i >= 0 && i < sh.n_chunk; }
+
+}  // namespace
+
+bool derive_shape(const wf_config* c, Shape* o, std::string* why) {
+  if (!c) return fail(why, "config is NULL");
+  if (c->S < 1 || c->S > WF_MAX_STAGES) return fail(why, "S must be in [1, 8]");
+  if (c->W < 0 || c->W > WF_MAX_PAGES) return fail(why, "W must be in [0, 48]");
+  if (c->W_store < -1 || c->W_store > WF_MAX_PAGES)
+    return fail(why, "W_store must be -1 or in [0, 48]");
+  if (c->anchor != 0 && c->anchor != 1) return fail(why, "anchor must be 0 or 1");
+  if (c->n_chunk < 1 || c->n_chunk > (1 << 20))
+    return fail(why, "n_chunk must be in [1, 2^20]");
+  if (c->F < 1 || c->Hh < 1 || c->Ww < 1) return fail(why, "F, Hh, Ww must be >= 1");
+  const int64_t n = int64_t(c->F) * c->Hh * c->Ww;
+  if (n > (1 << 24)) return fail(why, "tokens per chunk F*Hh*Ww must be <= 2^24");
+  if (c->n_heads < 1 || c->n_heads > 1024) return fail(why, "n_heads must be in [1, 1024]");
+  if (c->head_dim < 6 || c->head_dim > 512 || (c->head_dim & 1))
+    return fail(why, "head_dim must be even and in [6, 512]");
+  if (c->n_layers < 1 || c->n_layers > 4096) return fail(why, "n_layers must be in [1, 4096]");
+  if (c->dtype != WF_F32 && c->dtype != WF_BF16) return fail(why, "dtype must be WF_F32 or WF_BF16");
+  if (c->mask != WF_MASK_WAVE && c->mask != WF_MASK_ROLLING)
+    return fail(why, "mask must be WF_MASK_WAVE or WF_MASK_ROLLING");
+  if (c->reserved != 0) return fail(why, "reserved must be 0");
+  if (!(c->rope_theta >= 0.0) || !std::isfinite(c->rope_theta) ||
+      (c->rope_theta != 0.0 && c->rope_theta <= 1.0))
+    return fail(why, "rope_theta must be 0 (default) or > 1");
+  if (!(c->softmax_scale >= 0.0) || !std::isfinite(c->softmax_scale))
+    return fail(why, "softmax_scale must be finite and >= 0");
+
+  Shape s{};
+  s.S = c->S;
+  s.W = c->W;
+  s.Ws = c->W_store < 0 ? c->W + c->S : c->W_store;
+  s.Wmax = s.W > s.Ws ? s.W : s.Ws;
+  s.ring = s.Wmax + 2;
+  s.anchor = c->anchor;
+  s.n_chunk = c->n_chunk;
+  s.F = c->F;
+  s.Hh = c->Hh;
+  s.Ww = c->Ww;
+  s.H = c->n_heads;
+  s.D = c->head_dim;
+  s.L = c->n_layers;
+  s.N = static_cast<int>(n);
+  s.n_slots = 4 + s.Wmax + 2 * s.S;
+  // Longest context: anchor + history + store + every denoising chunk.
+  const int worst = 1 + s.Wmax + 1 + s.S;
+  if (worst > WF_MAX_PAGES) return fail(why, "anchor + max(W, W_store) + 1 + S exceeds 48 pages");
+  s.nh = s.D / 6;
+  s.nw = s.nh;
+  s.nt = s.D / 2 - 2 * s.nh;
+  s.n_frames = s.n_chunk * s.F;
+  s.dtype = c->dtype;
+  s.mask = c->mask;
+  s.theta = c->rope_theta == 0.0 ? 10000.0 : c->rope_theta;
+  s.scale = c->softmax_scale == 0.0 ? 1.0 / std::sqrt(double(s.D)) : c->softmax_scale;
+  s.elem = c->dtype == WF_BF16 ? 2 : 4;
+  size_t pe = 0, tmp = 0;
+  if (!mul_ok(size_t(2) * s.H, size_t(s.N), &pe) || !mul_ok(pe, size_t(s.D), &pe))
+    return fail(why, "page size overflows");
+  s.page_elems = pe;
+  if (!mul_ok(pe, s.elem, &tmp) || !mul_ok(tmp, size_t(s.L) * s.n_slots, &tmp))
+    return fail(why, "pool size overflows");
+  *o = s;
+  return true;
+}
+
+uint64_t config_hash(const wf_config& c) {
+  uint64_t h = 1469598103934665603ull;
+  auto mix = [&h](const void* p, size_t n) {
+    const unsigned char* b = static_cast<const unsigned char*>(p);
+    for (size_t i = 0; i < n; ++i) {
+      h ^= b[i];
+      h *= 1099511628211ull;
+    }
+  };
+  const int32_t ints[] = {c.S, c.W, c.W_store, c.anchor, c.n_chunk, c.F, c.Hh, c.Ww,
+                          c.n_heads, c.head_dim, c.n_layers, c.dtype, c.mask};
+  mix(ints, sizeof(ints));
+  mix(&c.rope_theta, sizeof(double));
+  mix(&c.softmax_scale, sizeof(double));
+  return h;
+}
+
+size_t pool_bytes(const Shape& sh) { return size_t(sh.L) * sh.n_slots * sh.page_elems * sh.elem; }
+size_t anchor_bytes(const Shape& sh) { return size_t(sh.L) * sh.page_elems * sh.elem; }
+size_t table_bytes(const Shape& sh) {
+  return (size_t(sh.n_frames) * sh.nt + size_t(sh.Hh) * sh.nh + size_t(sh.Ww) * sh.nw) *
+         2 * sizeof(float);
+}
+
+void build_plan(const Shape& sh, uint64_t hash, int64_t k, wf_plan* p) {
+  std::memset(p, 0, sizeof(*p));
+  p->k = k;
+  p->config_hash = hash;
+  p->S = sh.S;
+  const int S = sh.S;
+  const int64_t store_chunk = k - S;
+  const bool store_on = live(sh, store_chunk);
+  // Anchor: chunk 0, readable once it has been stored (round S), captured
+  // from the raw projections in that round (App. B.3).
+  const bool anchor_on = sh.anchor == 1 && k >= S + 1;
+  p->anchor.present = anchor_on;
+  p->anchor.capture = sh.anchor == 1 && k == S;
+  p->anchor.slot = anchor_on ? slot_anchor(k) : -1;
+  {
+    // Placed just before the oldest retained clean page when the window
+    // has slid past chunk 1.
+    const int64_t shift = k - S - sh.Wmax - 1;
+    p->anchor.frame0 = anchor_on ? static_cast<int>(sh.F * (shift > 0 ? shift : 0)) : -1;
+  }
+  p->evict_chunk = -1;
+  if (store_on && store_chunk - sh.Wmax >= sh.anchor) {
+    p->evict_chunk = static_cast<int>(store_chunk - sh.Wmax);
+  }
+
+  // Cells on the anti-diagonal k = i + s (Eq. 3).
+  for (int s = 0; s <= S; ++s) {
+    wf_cell& c = p->cells[s];
+    const int64_t i = k - s;
+    c.stage = s;
+    c.active = live(sh, i);
+    c.chunk = c.active ? static_cast<int>(i) : -1;
+    c.frame0 = c.active ? static_cast<int>(i * sh.F) : -1;
+    c.slot = !c.active ? -1 : (s == S ? slot_clean(sh, i) : slot_denoise(sh, k, s));
+    p->n_active += c.active;
+  }
+
+  // Ordered contexts (Eq. 5).
+  int64_t pages_total = 0;
+  for (int s = 0; s <= S; ++s) {
+    wf_group& g = p->groups[s];
+    g.stage = s;
+    if (!p->cells[s].active) continue;
+    int n = 0;
+    auto push = [&](int kind, int64_t chunk, int slot) {
+      g.kind[n] = kind;
+      g.chunk[n] = static_cast<int>(chunk);
+      g.slot[n] = slot;
+      ++n;
+    };
+    if (anchor_on) push(WF_KIND_ANCHOR, 0, slot_anchor(k));
+    const int window = s == S ? sh.Ws : sh.W;
+    int64_t lo = k - S - window;
+    if (lo < sh.anchor) lo = sh.anchor;
+    for (int64_t c = lo; c <= k - S - 1; ++c) push(WF_KIND_HISTORY, c, slot_clean(sh, c));
+    if (store_on) push(WF_KIND_STORE, store_chunk, slot_clean(sh, store_chunk));
+    if (s < S) {
+      // Denoising K/V by increasing stage j; WF reads j >= s, the
+      // Rolling-Forcing comparison reads every active stage.
+      const int j0 = sh.mask == WF_MASK_WAVE ? s : 0;
+      for (int j = j0; j < S; ++j) {
+        if (live(sh, k - j)) push(WF_KIND_DENOISE, k - j, slot_denoise(sh, k, j));
+      }
+    }
+    g.n_pages = n;
+    pages_total += n;
+  }
+
+  const double nhd = double(sh.N) * sh.H * sh.D;
+  p->kv_tokens = pages_total * sh.N;
+  p->flops = double(sh.L) * 4.0 * double(sh.N) * double(p->kv_tokens) * sh.D * sh.H;
+  // Publish traffic per layer: read q,k,v and write q_rot, K, Vt per active
+  // cell; read anchor_raw K, Vt and write the anchor slot when present;
+  // write anchor_raw K, Vt in the capture round.
+  double per_layer = 6.0 * p->n_active * nhd;
+  if (p->anchor.present) per_layer += 4.0 * nhd;
+  if (p->anchor.capture) per_layer += 2.0 * nhd;
+  p->publish_bytes = double(sh.L) * per_layer * double(sh.elem);
+}
+
+}  // namespace wf

@@ -1,0 +1,57 @@
+// Round scheduler and page allocator: host-only C++, no HIP dependency.
+//
+// The plan of round k is a pure function of (config, k).  Rules follow
+// "Wave Forcing: Towards Speed-of-Light Streaming Video Generation"
+// (arXiv 2611.00859): §3.1 Eq. 3 (cells and active set), Eq. 4 (mask),
+// Eq. 5 (context order), App. B.2 Eq. 13 (fixed double-buffered slots),
+// App. B.3 (store promotion, persistent anchor, store prefix budget).
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "wf.h"
+
+namespace wf {
+
+// Everything the library derives once from a validated wf_config.
+struct Shape {
+  int S, W, Ws, Wmax, ring, anchor, n_chunk;
+  int F, Hh, Ww, H, D, L, N;   // N = tokens per chunk
+  int n_slots;                 // 4 + Wmax + 2 S
+  int nt, nh, nw;              // RoPE pairs per axis (frame, row, column)
+  int n_frames;                // frame positions covered by the tables
+  int dtype, mask;
+  double theta, scale;
+  size_t elem;                 // bytes per element
+  size_t page_elems;           // 2 H N D
+};
+
+// Validates cfg (method-level rules only) and fills `out`.  Returns false
+// with a reason in `why` when the config is invalid.
+bool derive_shape(const wf_config* cfg, Shape* out, std::string* why);
+
+// FNV-1a over the config fields that change a plan or a launch.
+uint64_t config_hash(const wf_config& cfg);
+
+// Builds the plan of round k (caller checked 0 <= k < n_chunk + S).
+void build_plan(const Shape& sh, uint64_t hash, int64_t k, wf_plan* out);
+
+// Slot ring (closed form; ring = Wmax + 2):
+//   anchor -> k mod 2, clean chunk c -> 2 + c mod ring,
+//   denoising stage j of round k -> 2 + ring + (k mod 2) S + j.
+inline int slot_anchor(int64_t k) { return static_cast<int>(k & 1); }
+inline int slot_clean(const Shape& sh, int64_t c) {
+  return 2 + static_cast<int>(c % sh.ring);
+}
+inline int slot_denoise(const Shape& sh, int64_t k, int j) {
+  return 2 + sh.ring + static_cast<int>(k & 1) * sh.S + j;
+}
+
+// Bytes of caller buffers.
+size_t pool_bytes(const Shape& sh);
+size_t anchor_bytes(const Shape& sh);
+size_t table_bytes(const Shape& sh);
+
+}  // namespace wf

@@ -1,0 +1,331 @@
+// Host runtime behind include/wf.h: handle state, validation, RoPE tables,
+// kernel launches on the caller's stream.  Every check runs before any
+// device work; the library never allocates device memory and never
+// synchronises a stream (wf_bind's table upload is the one blocking copy).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "wf.h"
+#include "wf_kernels.h"
+#include "wf_plan.h"
+
+struct wf_handle {
+  wf_config cfg;
+  wf::Shape sh;
+  uint64_t hash = 0;
+  int64_t next_k = 0;
+  void* pool = nullptr;
+  void* anchor = nullptr;
+  void* tables = nullptr;
+  bool bound = false;
+  std::vector<uint8_t> published;  // per layer, current round
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+wf_status fail(wf_status s, const std::string& why) {
+  g_last_error = why;
+  return s;
+}
+
+wf_status ok() { return WF_OK; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Kernel support for a valid config (checked at bind time so that plans of
+// any valid config can be built without a device).
+wf_status check_supported(const wf::Shape& sh) {
+  if (sh.dtype == WF_BF16) {
+    if (sh.D != 64 && sh.D != 128)
+      return fail(WF_EUNSUPPORTED, "bf16 kernels need head_dim 64 or 128");
+    if (sh.N % 8 != 0) return fail(WF_EUNSUPPORTED, "bf16 kernels need tokens per chunk % 8 == 0");
+    // A 64-key tile then straddles at most one page boundary.
+    if (sh.N < 64) return fail(WF_EUNSUPPORTED, "bf16 kernels need tokens per chunk >= 64");
+  } else {
+    if (sh.D % 4 != 0 || sh.D > 128)
+      return fail(WF_EUNSUPPORTED, "fp32 kernels need head_dim % 4 == 0 and <= 128");
+    if (sh.N % 4 != 0) return fail(WF_EUNSUPPORTED, "fp32 kernels need tokens per chunk % 4 == 0");
+  }
+  return ok();
+}
+
+// Plan of the caller, checked against the handle: made for this config,
+// for the round the handle expects, and unmodified.
+wf_status check_plan(const wf_handle* h, const wf_plan* p, wf_plan* fresh) {
+  if (!h || !p) return fail(WF_EINVAL, "handle or plan is NULL");
+  if (p->config_hash != h->hash) return fail(WF_EORDER, "plan was made for another config");
+  if (p->k != h->next_k) {
+    return fail(WF_EORDER, "plan is for round " + std::to_string(p->k) + " but the handle expects round " +
+                               std::to_string(h->next_k));
+  }
+  wf::build_plan(h->sh, h->hash, p->k, fresh);
+  if (std::memcmp(fresh, p, sizeof(wf_plan)) != 0) return fail(WF_EINVAL, "plan contents were modified");
+  return ok();
+}
+
+size_t stage_bytes(const wf::Shape& sh) {
+  return size_t(sh.S + 1) * size_t(sh.N) * size_t(sh.H) * size_t(sh.D) * sh.elem;
+}
+
+char* layer_ptr(void* base, size_t per_layer, int layer) {
+  return static_cast<char*>(base) + per_layer * size_t(layer);
+}
+
+wf_status do_publish(wf_handle* h, const wf_plan& p, int layer, const void* q, const void* k,
+                     const void* v, void* q_rot, hipStream_t stream) {
+  const wf::Shape& sh = h->sh;
+  wf::PublishArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.q_rot = q_rot;
+  a.pool = layer_ptr(h->pool, size_t(sh.n_slots) * sh.page_elems * sh.elem, layer);
+  a.anchor_raw = layer_ptr(h->anchor, sh.page_elems * sh.elem, layer);
+  a.rope = static_cast<const float2*>(h->tables);
+  a.page_elems = static_cast<int64_t>(sh.page_elems);
+  a.N = sh.N;
+  a.H = sh.H;
+  a.D = sh.D;
+  a.F = sh.F;
+  a.Hh = sh.Hh;
+  a.Ww = sh.Ww;
+  a.nt = sh.nt;
+  a.nh = sh.nh;
+  a.nw = sh.nw;
+  a.n_frames = sh.n_frames;
+  int n = 0;
+  for (int s = 0; s <= sh.S; ++s) {
+    const wf_cell& c = p.cells[s];
+    if (!c.active) continue;
+    const bool capture = s == sh.S && p.anchor.capture;
+    a.task[n++] = {s, c.slot, c.frame0, capture ? wf::TASK_CAPTURE : wf::TASK_CELL};
+  }
+  if (p.anchor.present) a.task[n++] = {0, p.anchor.slot, p.anchor.frame0, wf::TASK_ANCHOR};
+  a.n_tasks = n;
+  (void)hipGetLastError();
+  const hipError_t e = wf::launch_publish(a, sh.dtype, stream);
+  if (e != hipSuccess) return fail(WF_EDEVICE, std::string("publish launch: ") + hipGetErrorString(e));
+  h->published[layer] = 1;
+  return ok();
+}
+
+wf_status do_attention(wf_handle* h, const wf_plan& p, int layer, const void* q_rot, void* out,
+                       hipStream_t stream) {
+  const wf::Shape& sh = h->sh;
+  wf::AttnArgs a{};
+  a.q_rot = q_rot;
+  a.out = out;
+  a.pool = layer_ptr(h->pool, size_t(sh.n_slots) * sh.page_elems * sh.elem, layer);
+  a.page_elems = static_cast<int64_t>(sh.page_elems);
+  a.N = sh.N;
+  a.H = sh.H;
+  a.D = sh.D;
+  a.scale_log2e = static_cast<float>(sh.scale * 1.4426950408889634);
+  const int bm = sh.dtype == WF_BF16 ? wf::kAttnBM_bf16 : wf::kAttnBM_f32;
+  a.q_tiles = (sh.N + bm - 1) / bm;
+  // Active groups, longest context first (ties: lower stage first).
+  int order[WF_MAX_GROUPS];
+  int ng = 0;
+  for (int s = 0; s <= sh.S; ++s)
+    if (p.groups[s].n_pages > 0) order[ng++] = s;
+  std::stable_sort(order, order + ng,
+                   [&](int x, int y) { return p.groups[x].n_pages > p.groups[y].n_pages; });
+  int item = 0;
+  for (int i = 0; i < ng; ++i) {
+    const wf_group& g = p.groups[order[i]];
+    wf::AttnGroup& o = a.grp[i];
+    o.stage = g.stage;
+    o.n_pages = g.n_pages;
+    o.item0 = item;
+    for (int j = 0; j < g.n_pages; ++j) o.slot[j] = static_cast<uint16_t>(g.slot[j]);
+    item += sh.H * a.q_tiles;
+  }
+  a.n_groups = ng;
+  a.n_items = item;
+  (void)hipGetLastError();
+  const hipError_t e = wf::launch_attention(a, sh.dtype, stream);
+  if (e != hipSuccess) return fail(WF_EDEVICE, std::string("attention launch: ") + hipGetErrorString(e));
+  return ok();
+}
+
+wf_status check_layer_call(const wf_handle* h, int32_t layer) {
+  if (layer < 0 || layer >= h->sh.L) return fail(WF_EINVAL, "layer out of range");
+  if (!h->bound) return fail(WF_EINVAL, "handle is not bound (call wf_bind first)");
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* wf_strerror(wf_status s) {
+  switch (s) {
+    case WF_OK: return "ok";
+    case WF_EINVAL: return "invalid argument";
+    case WF_ERANGE: return "round out of range";
+    case WF_EORDER: return "call out of order";
+    case WF_ESMALL: return "buffer too small";
+    case WF_EDEVICE: return "device error";
+    case WF_EUNSUPPORTED: return "unsupported configuration";
+  }
+  return "unknown status";
+}
+
+const char* wf_last_error(void) { return g_last_error.c_str(); }
+
+wf_status wf_create(const wf_config* cfg, wf_handle** out) {
+  if (!out) return fail(WF_EINVAL, "out is NULL");
+  *out = nullptr;
+  wf::Shape sh;
+  std::string why;
+  if (!wf::derive_shape(cfg, &sh, &why)) return fail(WF_EINVAL, why);
+  wf_handle* h = new (std::nothrow) wf_handle();
+  if (!h) return fail(WF_EINVAL, "out of host memory");
+  h->cfg = *cfg;
+  h->sh = sh;
+  h->hash = wf::config_hash(*cfg);
+  h->published.assign(size_t(sh.L), 0);
+  *out = h;
+  return ok();
+}
+
+void wf_destroy(wf_handle* h) { delete h; }
+
+wf_status wf_pool_bytes(const wf_config* cfg, size_t* pool, size_t* anchor, size_t* tables) {
+  wf::Shape sh;
+  std::string why;
+  if (!wf::derive_shape(cfg, &sh, &why)) return fail(WF_EINVAL, why);
+  if (pool) *pool = wf::pool_bytes(sh);
+  if (anchor) *anchor = wf::anchor_bytes(sh);
+  if (tables) *tables = wf::table_bytes(sh);
+  return ok();
+}
+
+wf_status wf_bind(wf_handle* h, void* d_pool, size_t pool_bytes, void* d_anchor_raw,
+                  size_t anchor_bytes, void* d_tables, size_t table_bytes) {
+  if (!h) return fail(WF_EINVAL, "handle is NULL");
+  if (!d_pool || !d_anchor_raw || !d_tables) return fail(WF_EINVAL, "device buffer is NULL");
+  const wf::Shape& sh = h->sh;
+  if (pool_bytes < wf::pool_bytes(sh)) return fail(WF_ESMALL, "slot pool smaller than wf_pool_bytes");
+  if (anchor_bytes < wf::anchor_bytes(sh)) return fail(WF_ESMALL, "anchor buffer smaller than wf_pool_bytes");
+  if (table_bytes < wf::table_bytes(sh)) return fail(WF_ESMALL, "table buffer smaller than wf_pool_bytes");
+  if (!aligned16(d_pool) || !aligned16(d_anchor_raw) || !aligned16(d_tables))
+    return fail(WF_EINVAL, "device buffers must be 16-byte aligned");
+  const wf_status sup = check_supported(sh);
+  if (sup != WF_OK) return sup;
+
+  // cos/sin of every (position, pair) per axis, computed in fp64.
+  std::vector<float> tab(wf::table_bytes(sh) / sizeof(float));
+  size_t at = 0;
+  auto axis = [&](int n_pos, int n_pairs) {
+    for (int pos = 0; pos < n_pos; ++pos) {
+      for (int m = 0; m < n_pairs; ++m) {
+        const double w = std::pow(sh.theta, -double(m) / double(n_pairs));
+        const double ang = double(pos) * w;
+        tab[at++] = static_cast<float>(std::cos(ang));
+        tab[at++] = static_cast<float>(std::sin(ang));
+      }
+    }
+  };
+  axis(sh.n_frames, sh.nt);
+  axis(sh.Hh, sh.nh);
+  axis(sh.Ww, sh.nw);
+  const hipError_t e = hipMemcpy(d_tables, tab.data(), tab.size() * sizeof(float), hipMemcpyHostToDevice);
+  if (e != hipSuccess) return fail(WF_EDEVICE, std::string("table upload: ") + hipGetErrorString(e));
+  h->pool = d_pool;
+  h->anchor = d_anchor_raw;
+  h->tables = d_tables;
+  h->bound = true;
+  return ok();
+}
+
+wf_status wf_round_plan(const wf_handle* h, int64_t k, wf_plan* out) {
+  if (!h || !out) return fail(WF_EINVAL, "handle or out is NULL");
+  if (k < 0 || k >= int64_t(h->sh.n_chunk) + h->sh.S)
+    return fail(WF_ERANGE, "round " + std::to_string(k) + " outside [0, n_chunk + S)");
+  wf::build_plan(h->sh, h->hash, k, out);
+  return ok();
+}
+
+wf_status wf_next_round(const wf_handle* h, int64_t* k) {
+  if (!h || !k) return fail(WF_EINVAL, "handle or out is NULL");
+  *k = h->next_k;
+  return ok();
+}
+
+wf_status wf_reset(wf_handle* h) {
+  if (!h) return fail(WF_EINVAL, "handle is NULL");
+  h->next_k = 0;
+  std::fill(h->published.begin(), h->published.end(), 0);
+  return ok();
+}
+
+wf_status wf_kv_publish(wf_handle* h, const wf_plan* plan, int32_t layer, const void* d_q,
+                        const void* d_k, const void* d_v, void* d_q_rot, void* stream) {
+  wf_plan p;
+  wf_status s = check_plan(h, plan, &p);
+  if (s != WF_OK) return s;
+  if ((s = check_layer_call(h, layer)) != WF_OK) return s;
+  if (!d_q || !d_k || !d_v || !d_q_rot) return fail(WF_EINVAL, "q, k, v or q_rot is NULL");
+  if (!aligned16(d_q) || !aligned16(d_k) || !aligned16(d_v) || !aligned16(d_q_rot))
+    return fail(WF_EINVAL, "q, k, v and q_rot must be 16-byte aligned");
+  return do_publish(h, p, layer, d_q, d_k, d_v, d_q_rot, static_cast<hipStream_t>(stream));
+}
+
+wf_status wf_wave_attention(wf_handle* h, const wf_plan* plan, int32_t layer, const void* d_q_rot,
+                            void* d_out, void* stream) {
+  wf_plan p;
+  wf_status s = check_plan(h, plan, &p);
+  if (s != WF_OK) return s;
+  if ((s = check_layer_call(h, layer)) != WF_OK) return s;
+  if (!h->published[layer]) return fail(WF_EORDER, "layer not published in this round");
+  if (!d_q_rot || !d_out) return fail(WF_EINVAL, "q_rot or out is NULL");
+  if (!aligned16(d_q_rot) || !aligned16(d_out))
+    return fail(WF_EINVAL, "q_rot and out must be 16-byte aligned");
+  return do_attention(h, p, layer, d_q_rot, d_out, static_cast<hipStream_t>(stream));
+}
+
+wf_status wf_round_commit(wf_handle* h, const wf_plan* plan) {
+  wf_plan p;
+  const wf_status s = check_plan(h, plan, &p);
+  if (s != WF_OK) return s;
+  for (int l = 0; l < h->sh.L; ++l)
+    if (!h->published[l]) return fail(WF_EORDER, "layer " + std::to_string(l) + " not published");
+  h->next_k += 1;
+  std::fill(h->published.begin(), h->published.end(), 0);
+  return ok();
+}
+
+wf_status wf_round(wf_handle* h, const wf_plan* plan, const void* d_q, const void* d_k,
+                   const void* d_v, void* d_q_rot, void* d_out, void* stream) {
+  wf_plan p;
+  wf_status s = check_plan(h, plan, &p);
+  if (s != WF_OK) return s;
+  if (!h->bound) return fail(WF_EINVAL, "handle is not bound (call wf_bind first)");
+  if (!d_q || !d_k || !d_v || !d_q_rot || !d_out) return fail(WF_EINVAL, "a tensor pointer is NULL");
+  if (!aligned16(d_q) || !aligned16(d_k) || !aligned16(d_v) || !aligned16(d_q_rot) || !aligned16(d_out))
+    return fail(WF_EINVAL, "tensors must be 16-byte aligned");
+  const size_t per_layer = stage_bytes(h->sh);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  for (int l = 0; l < h->sh.L; ++l) {
+    s = do_publish(h, p, l, layer_ptr(const_cast<void*>(d_q), per_layer, l),
+                   layer_ptr(const_cast<void*>(d_k), per_layer, l),
+                   layer_ptr(const_cast<void*>(d_v), per_layer, l), layer_ptr(d_q_rot, per_layer, l), st);
+    if (s != WF_OK) return s;
+    s = do_attention(h, p, l, layer_ptr(d_q_rot, per_layer, l), layer_ptr(d_out, per_layer, l), st);
+    if (s != WF_OK) return s;
+  }
+  h->next_k += 1;
+  std::fill(h->published.begin(), h->published.end(), 0);
+  return ok();
+}
+
+}  // extern "C"

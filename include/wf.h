@@ -1,0 +1,230 @@
+/*
+ * wf.h -- C ABI of the MI355X (gfx950) wavefront-round library.
+ *
+ * One call sequence runs one round of Wave Forcing's chunk-wise causal
+ * attention ("Wave Forcing: Towards Speed-of-Light Streaming Video
+ * Generation", arXiv 2611.00859; cited below as WF):
+ *
+ *   wf_round_plan      which cells are active, which key pages each query
+ *                      group reads and in which order, which slot every page
+ *                      lives in                      (WF §3.1 Eq. 3-5, App. B.3)
+ *   wf_kv_publish      per layer: 3D-RoPE on q and k, K/V written straight into
+ *                      their fixed attention slots  (WF §4.1 Eq. 8, App. B.2 Eq. 13)
+ *   wf_wave_attention  per layer: every active group attends to its ordered
+ *                      context under M_WF(s,j) = 1[j >= s] in one launch
+ *                                                    (WF §3.1 Eq. 4-5, §4.2 Eq. 10)
+ *   wf_round_commit    store page promoted to history, round counter advanced
+ *                                                    (WF App. B.3)
+ *   wf_round           all layers (publish, attention) then commit
+ *
+ * Conventions
+ *   - Every call returns a wf_status; 0 is success, negative is an error.
+ *     Nothing is thrown across the ABI.  wf_last_error() gives a
+ *     thread-local human-readable detail for the last failing call.
+ *   - All validation happens before any device work; a failing call has
+ *     launched nothing.  Errors of asynchronous device execution surface at
+ *     the caller's next synchronisation.
+ *   - The caller owns all device memory (inputs, outputs, the slot pool,
+ *     the anchor store and the RoPE tables) and the stream.  The library
+ *     never allocates device memory and never synchronises the stream.  The
+ *     handle holds host state only.  Device pointers must stay valid until
+ *     the stream work that uses them has completed.
+ *   - Streams are passed as `void*` holding a hipStream_t (NULL = the null
+ *     stream), so this header needs no HIP headers.
+ *   - Chunk, stage and layer indices are zero-based (WF numbers layers from
+ *     one; App. B.8 "Index conventions").
+ *   - Stage S is the store cell (k - S, S); stages 0..S-1 are denoising.
+ *
+ * Device layouts (element type = dtype: fp32 or bf16; D = head_dim,
+ * H = n_heads, N = tokens per chunk = F * Hh * Ww, token n at frame
+ * n / (Hh Ww), row (n / Ww) % Hh, column n % Ww):
+ *   q, k, v, q_rot, out   per layer [S+1][N][H][D], indexed by stage; the
+ *                         store is stage S; rows of inactive stages are
+ *                         neither read nor written.  wf_round takes
+ *                         [L][S+1][N][H][D].
+ *   page                  one chunk's keys and values for one layer:
+ *                         K  [H][N][D]   (RoPE applied)
+ *                         Vt [H][D][N]   (values, transposed: keys contiguous)
+ *                         page_elems = 2 * H * N * D.
+ *   pool                  [L][n_slots] pages, n_slots = 4 + max(W, W_store) + 2 S.
+ *   anchor_raw            [L] pages holding chunk 0's unrotated K and its Vt.
+ *   tables                fp32 cos/sin pairs written by wf_bind.
+ */
+#ifndef WF_H
+#define WF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WF_MAX_STAGES 8                     /* S <= 8 denoising stages     */
+#define WF_MAX_GROUPS (WF_MAX_STAGES + 1)   /* + the store                 */
+#define WF_MAX_PAGES 48                     /* key pages per query group   */
+
+typedef enum {
+  WF_OK = 0,
+  WF_EINVAL = -1,       /* bad argument, config or pointer                  */
+  WF_ERANGE = -2,       /* round index outside [0, n_chunk + S)             */
+  WF_EORDER = -3,       /* plan not for this handle / not the next round /
+                           attention before publish / commit before publish */
+  WF_ESMALL = -4,       /* a caller buffer is smaller than required         */
+  WF_EDEVICE = -5,      /* a HIP call or kernel launch failed               */
+  WF_EUNSUPPORTED = -6  /* valid config without a kernel instance           */
+} wf_status;
+
+typedef enum { WF_F32 = 0, WF_BF16 = 1 } wf_dtype;
+
+typedef enum {
+  WF_MASK_WAVE = 0,    /* M_WF(s,j) = 1[j >= s]                 (WF §3.1 Eq. 4) */
+  WF_MASK_ROLLING = 1  /* every active denoising chunk reads every other one
+                          (Rolling Forcing's window, WF §3.1; comparison only) */
+} wf_mask;
+
+typedef enum {
+  WF_KIND_ANCHOR = 0,  /* first clean chunk, persistent            (App. B.3) */
+  WF_KIND_HISTORY = 1, /* bounded clean history                    (Eq. 5)    */
+  WF_KIND_STORE = 2,   /* live store page of this round            (Eq. 5)    */
+  WF_KIND_DENOISE = 3  /* denoising chunk of this round            (Eq. 5)    */
+} wf_kind;
+
+/* Round shape.  All fields are read by wf_create; the handle keeps a copy. */
+typedef struct {
+  int32_t S;          /* denoising steps; round width is S + 1 (WF §2 Eq. 2)  */
+  int32_t W;          /* clean-history pages a denoising query reads           */
+  int32_t W_store;    /* history pages the store reads; -1 = W + S, i.e. the
+                         same (W + S + 2)-chunk context budget as stage 0      */
+  int32_t anchor;     /* 1 = keep chunk 0 as persistent anchor, 0 = none       */
+  int32_t n_chunk;    /* chunks in the request (>= 1); rounds = n_chunk + S    */
+  int32_t F, Hh, Ww;  /* latent frames per chunk, token rows, token columns    */
+  int32_t n_heads;    /* H                                                    */
+  int32_t head_dim;   /* D (even, >= 6)                                       */
+  int32_t n_layers;   /* L                                                    */
+  int32_t dtype;      /* wf_dtype of q/k/v/q_rot/out and of the pages          */
+  int32_t mask;       /* wf_mask                                              */
+  int32_t reserved;   /* must be 0                                            */
+  double rope_theta;  /* RoPE base; 0 selects 10000                            */
+  double softmax_scale; /* 0 selects 1/sqrt(head_dim)                          */
+} wf_config;
+
+/* One cell (k - stage, stage) of the round. */
+typedef struct {
+  int32_t stage;
+  int32_t chunk;   /* k - stage, or -1 when inactive                           */
+  int32_t active;  /* 1 if 0 <= chunk < n_chunk                                */
+  int32_t slot;    /* slot its K/V page is published into, or -1              */
+  int32_t frame0;  /* first latent-frame position F * chunk, or -1            */
+} wf_cell;
+
+/* Ordered context of the query group of one stage (WF §3.1 Eq. 5). */
+typedef struct {
+  int32_t stage;
+  int32_t n_pages;                 /* 0 when the cell is inactive            */
+  int32_t slot[WF_MAX_PAGES];      /* pool slot of each page, context order  */
+  int32_t chunk[WF_MAX_PAGES];     /* logical chunk id of each page          */
+  int32_t kind[WF_MAX_PAGES];      /* wf_kind of each page                   */
+} wf_group;
+
+typedef struct {
+  int32_t present;  /* anchor page is read this round (k > S, anchor on)      */
+  int32_t slot;     /* k mod 2 when present, else -1                          */
+  int32_t frame0;   /* frame position the anchor key is rotated to, or -1     */
+  int32_t capture;  /* 1 in round S: chunk 0's raw K/V is saved               */
+} wf_anchor;
+
+/* Plain-old-data plan of one round; a pure function of (config, k). */
+typedef struct {
+  int64_t k;
+  uint64_t config_hash;            /* identifies the config it was made for  */
+  int32_t S;
+  int32_t n_active;                /* active cells, store included           */
+  wf_cell cells[WF_MAX_GROUPS];    /* index = stage                          */
+  wf_group groups[WF_MAX_GROUPS];  /* index = query stage                    */
+  wf_anchor anchor;
+  int32_t evict_chunk;             /* leaves the retained window after the
+                                      round's store is promoted, or -1       */
+  int32_t reserved;
+  int64_t kv_tokens;               /* key tokens summed over groups, 1 layer */
+  double flops;                    /* attention flops, all layers: 4 N D H
+                                      per key token (QK^T and PV)            */
+  double publish_bytes;            /* publish HBM bytes, all layers          */
+} wf_plan;
+
+typedef struct wf_handle wf_handle;
+
+/* Text for a status code (static storage). */
+const char* wf_strerror(wf_status status);
+
+/* Detail of the last failing call on this thread ("" if none). */
+const char* wf_last_error(void);
+
+/* Validate `cfg` and create a handle (host memory only; no device calls).
+ * WF_EINVAL for an invalid config or a NULL pointer. */
+wf_status wf_create(const wf_config* cfg, wf_handle** out);
+
+/* Free a handle (NULL is ignored).  Device memory stays the caller's. */
+void wf_destroy(wf_handle* h);
+
+/* Bytes the caller must allocate for the slot pool, the anchor store and
+ * the RoPE tables of `cfg`.  Any output pointer may be NULL. */
+wf_status wf_pool_bytes(const wf_config* cfg, size_t* pool_bytes,
+                        size_t* anchor_bytes, size_t* table_bytes);
+
+/* Attach caller-owned device buffers and upload the RoPE tables (computed
+ * on the host in fp64, stored as fp32) with a synchronous copy.  Sizes are
+ * checked first (WF_ESMALL), then kernel support for the config
+ * (WF_EUNSUPPORTED: bf16 needs head_dim 64 or 128, N % 8 == 0, N >= 64; fp32
+ * needs head_dim % 4 == 0, head_dim <= 128 and N % 4 == 0).  Buffers must
+ * be 16-byte aligned.  The handle keeps the pointers, not the memory. */
+wf_status wf_bind(wf_handle* h, void* d_pool, size_t pool_bytes,
+                  void* d_anchor_raw, size_t anchor_bytes,
+                  void* d_tables, size_t table_bytes);
+
+/* Plan round k (host only, no device calls; valid before wf_bind).
+ * WF_ERANGE if k is outside [0, n_chunk + S). */
+wf_status wf_round_plan(const wf_handle* h, int64_t k, wf_plan* out);
+
+/* Round index the handle expects next (0 after create / reset). */
+wf_status wf_next_round(const wf_handle* h, int64_t* k);
+
+/* Start a new request at round 0.  Page contents become meaningless. */
+wf_status wf_reset(wf_handle* h);
+
+/* Layer `layer` of the round's producer step (WF §4.1 Eq. 8 P_{s,l}, App.
+ * B.2 Eq. 13): for every active cell, q_rot = RoPE3D(q), the cell's page
+ * slot gets K = RoPE3D(k) and Vt = v^T.  In round S the store cell's raw k
+ * and v^T are also kept in anchor_raw; when the anchor is present its slot
+ * gets RoPE3D(anchor K, anchor position) and the anchor Vt.
+ * d_q/d_k/d_v: this layer's [S+1][N][H][D] inputs (read only);
+ * d_q_rot: this layer's [S+1][N][H][D] output.  Enqueued on `stream`.
+ * WF_EORDER if the plan is not the handle's next round or was made for
+ * another config; WF_EINVAL if unbound or a pointer is NULL. */
+wf_status wf_kv_publish(wf_handle* h, const wf_plan* plan, int32_t layer,
+                        const void* d_q, const void* d_k, const void* d_v,
+                        void* d_q_rot, void* stream);
+
+/* Layer `layer` of the round's attention (WF §3.1 Eq. 4-5): for every
+ * active query group g and head, out = softmax(scale * Q K^T) V over the
+ * group's key pages concatenated in plan order.  One launch covers all
+ * groups.  d_q_rot: [S+1][N][H][D] from wf_kv_publish; d_out: [S+1][N][H][D].
+ * WF_EORDER if this layer was not published in this round. */
+wf_status wf_wave_attention(wf_handle* h, const wf_plan* plan, int32_t layer,
+                            const void* d_q_rot, void* d_out, void* stream);
+
+/* End the round (WF App. B.3): requires every layer published; advances
+ * the expected round.  Host only: the store page is promoted in place. */
+wf_status wf_round_commit(wf_handle* h, const wf_plan* plan);
+
+/* Whole round: for l = 0..L-1 publish(l) then attention(l), then commit.
+ * d_q/d_k/d_v/d_q_rot/d_out are [L][S+1][N][H][D]. */
+wf_status wf_round(wf_handle* h, const wf_plan* plan,
+                   const void* d_q, const void* d_k, const void* d_v,
+                   void* d_q_rot, void* d_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WF_H */

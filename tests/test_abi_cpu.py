@@ -1,0 +1,157 @@
+"""C-ABI checks that need no GPU: exports, plan parity, error paths.
+
+``wf_round_plan`` is host-only integer code, so the C library's plans are
+compared here, field by field and bit-exactly, with the independent oracle
+(``oracle/wf_plan.py``).  Error paths are forced from the host; every failing
+call returns before any device work.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from chunk_causal_dit_round_amd import wf
+from chunk_causal_dit_round_amd.workloads import ALL, TINY_FP32, WAN13B_4STEP
+from oracle import wf_plan as P
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "wf.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(wf_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = header_functions()
+    assert len(names) == 13, names
+    lib = ctypes.CDLL(wf.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def oracle_cfg(c):
+    return P.Config(S=c.S, W=c.W, W_store=c.W_store, anchor=c.anchor, n_chunk=c.n_chunk,
+                    F=c.F, Hh=c.Hh, Ww=c.Ww, n_heads=c.n_heads, head_dim=c.head_dim,
+                    n_layers=c.n_layers, mask=c.mask)
+
+
+CONFIGS = [wf.make_config(S, W, N, 3, 4, 6, 2, 64, 3, W_store=Ws, anchor=A, mask=m, dtype=wf.WF_F32)
+           for S in (1, 2, 3, 4, 5, 8) for N in (1, 2, 5, 9, 16)
+           for (W, Ws) in ((0, -1), (2, -1), (4, 4), (6, 2), (3, 0)) for A in (0, 1)
+           for m in (wf.WF_MASK_WAVE, wf.WF_MASK_ROLLING)]
+CONFIGS += [w.config() for w in ALL.values()]
+
+
+@pytest.mark.parametrize("cfg", CONFIGS, ids=lambda c: f"S{c.S}W{c.W}/{c.W_store}A{c.anchor}N{c.n_chunk}m{c.mask}H{c.n_heads}")
+def test_plan_parity_with_oracle(cfg):
+    h = wf.wf_create(cfg)
+    oc = oracle_cfg(cfg)
+    try:
+        for k in range(oc.n_rounds):
+            got = wf.plan_to_dict(wf.wf_round_plan(h, k))
+            want = P.plan(oc, k)
+            for key in ("k", "cells", "groups", "anchor", "evict", "kv_tokens", "n_active"):
+                assert got[key] == want[key], (k, key)
+            assert got["flops"] == want["flops"]
+    finally:
+        wf.wf_destroy(h)
+
+
+def test_plan_numbers_1p3b_4step():
+    h = wf.wf_create(WAN13B_4STEP.config())
+    p = wf.wf_round_plan(h, 13)
+    assert [p.groups[s].n_pages for s in range(5)] == [10, 9, 8, 7, 10]
+    assert abs(p.flops - 1.7763e14) / 1.7763e14 < 1e-4
+    # publish: 5 cells x (q,k,v in; q_rot,K,Vt out) + anchor (2 in, 2 out), 30 layers
+    nhd2 = 4680 * 12 * 128 * 2
+    assert p.publish_bytes == 30 * (30 + 4) * nhd2
+    wf.wf_destroy(h)
+
+
+def test_pool_bytes():
+    cfg = WAN13B_4STEP.config()
+    pool, anc, tab = wf.wf_pool_bytes(cfg)
+    page = 2 * 4680 * 12 * 128 * 2
+    assert pool == 30 * 20 * page
+    assert anc == 30 * page
+    assert tab == (133 * 3 * 22 + 30 * 21 + 52 * 21) * 8
+
+
+BAD = [dict(S=0), dict(S=9), dict(W=-1), dict(W_store=-2), dict(anchor=2), dict(n_chunk=0),
+       dict(F=0), dict(n_heads=0), dict(head_dim=7), dict(head_dim=4), dict(n_layers=0),
+       dict(dtype=5), dict(mask=3), dict(reserved=1), dict(rope_theta=-1.0),
+       dict(rope_theta=0.5), dict(softmax_scale=-1.0), dict(W=40, S=8)]
+
+
+@pytest.mark.parametrize("bad", BAD, ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
+def test_invalid_config_rejected(bad):
+    cfg = TINY_FP32.config()
+    for k, v in bad.items():
+        setattr(cfg, k, v)
+    assert wf.status_of(wf.wf_create, cfg) == wf.WF_EINVAL
+    assert wf.wf_last_error() != ""
+    assert wf.status_of(wf.wf_pool_bytes, cfg) == wf.WF_EINVAL
+
+
+def test_round_range_and_order_errors():
+    cfg = TINY_FP32.config()
+    h = wf.wf_create(cfg)
+    h2 = wf.wf_create(WAN13B_4STEP.config())
+    try:
+        assert wf.status_of(wf.wf_round_plan, h, -1) == wf.WF_ERANGE
+        assert wf.status_of(wf.wf_round_plan, h, 8) == wf.WF_ERANGE
+        assert wf.wf_next_round(h) == 0
+        p1 = wf.wf_round_plan(h, 1)
+        p0 = wf.wf_round_plan(h, 0)
+        other = wf.wf_round_plan(h2, 0)
+        # not the next round / another config: rejected before anything else
+        for fn, args in ((wf.wf_kv_publish, (0, 16, 16, 16, 16)),
+                         (wf.wf_wave_attention, (0, 16, 16)),
+                         (wf.wf_round, (16, 16, 16, 16, 16))):
+            assert wf.status_of(fn, h, p1, *args, stream=0) == wf.WF_EORDER
+            assert wf.status_of(fn, h, other, *args, stream=0) == wf.WF_EORDER
+            # right round, but the handle is not bound
+            assert wf.status_of(fn, h, p0, *args, stream=0) == wf.WF_EINVAL
+        assert wf.status_of(wf.wf_round_commit, h, p1) == wf.WF_EORDER
+        assert wf.status_of(wf.wf_round_commit, h, p0) == wf.WF_EORDER   # nothing published
+        # a modified plan is refused
+        bad = wf.wf_round_plan(h, 0)
+        bad.groups[0].slot[0] = 99
+        assert wf.status_of(wf.wf_round_commit, h, bad) == wf.WF_EINVAL
+        assert wf.status_of(wf.wf_reset, h) == wf.WF_OK
+    finally:
+        wf.wf_destroy(h)
+        wf.wf_destroy(h2)
+
+
+def test_bind_errors_before_device_work():
+    cfg = TINY_FP32.config()
+    h = wf.wf_create(cfg)
+    pb, ab, tb = wf.wf_pool_bytes(cfg)
+    fake = 1 << 20    # never dereferenced: every case fails before device work
+    try:
+        assert wf.status_of(wf.wf_bind, h, fake, pb - 1, fake, ab, fake, tb) == wf.WF_ESMALL
+        assert wf.status_of(wf.wf_bind, h, fake, pb, fake, ab - 1, fake, tb) == wf.WF_ESMALL
+        assert wf.status_of(wf.wf_bind, h, fake, pb, fake, ab, fake, tb - 1) == wf.WF_ESMALL
+        assert wf.status_of(wf.wf_bind, h, None, pb, fake, ab, fake, tb) == wf.WF_EINVAL
+        assert wf.status_of(wf.wf_bind, h, fake + 4, pb, fake, ab, fake, tb) == wf.WF_EINVAL
+    finally:
+        wf.wf_destroy(h)
+    for w in (WAN13B_4STEP.with_(head_dim=96), WAN13B_4STEP.with_(Ww=51),
+              WAN13B_4STEP.with_(F=1, Hh=7, Ww=8),
+              TINY_FP32.with_(head_dim=66), TINY_FP32.with_(head_dim=256)):
+        cfg = w.config()
+        h = wf.wf_create(cfg)
+        pb, ab, tb = wf.wf_pool_bytes(cfg)
+        assert wf.status_of(wf.wf_bind, h, fake, pb, fake, ab, fake, tb) == wf.WF_EUNSUPPORTED
+        wf.wf_destroy(h)
+
+
+def test_strerror():
+    for s in range(0, -7, -1):
+        assert wf.wf_strerror(s) and wf.wf_strerror(s) != "unknown status"
+    assert wf.wf_strerror(-99) == "unknown status"

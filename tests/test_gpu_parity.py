@@ -1,0 +1,139 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Small shapes are compared element by element over every round of a request
+(several query and key tiles, ragged tails, fill, steady state, drain,
+anchor re-rotation, ring wrap).  Full Wan2.1 shapes are compared on sampled
+query rows (each against its full key list) and on whole pages.
+
+Tolerances: attention max-abs error 2e-2 for bf16 inputs, 1e-4 for fp32
+inputs; RoPE'd q/k within one bf16 unit in the last place (fp32: 2e-6
+relative); values and every plan field bit-exact.
+"""
+
+import gc
+
+import pytest
+import torch
+
+from chunk_causal_dit_round_amd import wf
+from chunk_causal_dit_round_amd.workloads import (TINY_FP32, WAN13B_4STEP, WAN13B_5STEP,
+                                                  WAN13B_5STEP_ROLLING, WAN14B_4STEP, Workload)
+from wfcheck import Rollout, check_attention, check_publish
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _free_memory():
+    yield
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def full_rollout(w, check_rows=None, check_rounds=None, layers=None, mode="round"):
+    ro = Rollout(w)
+    try:
+        for k in range(w.n_chunk + w.S):
+            ro.run(k, mode=mode)
+            if check_rounds is None or k in check_rounds:
+                for layer in (range(w.n_layers) if layers is None else layers):
+                    check_publish(ro, k, layer)
+                    check_attention(ro, k, layer, rows=check_rows)
+    finally:
+        ro.close()
+
+
+def test_tiny_fp32_every_round():
+    _log("tiny fp32: 8 rounds")
+    full_rollout(TINY_FP32)
+
+
+def test_tiny_fp32_long_rollout_ring_wrap_and_anchor_shift():
+    w = TINY_FP32.with_(name="tiny_fp32_long", n_chunk=16)
+    _log("tiny fp32 long: 18 rounds")
+    full_rollout(w)
+
+
+SMALL_BF16 = [
+    # several query tiles + ragged tail (360 = 2*128 + 104), keys straddle pages
+    Workload("bf16_s4_n360", S=4, W=4, n_chunk=12, F=3, Hh=10, Ww=12, n_heads=3,
+             head_dim=128, n_layers=2),
+    # one partial query tile; 72-key pages straddle every 64-key tile
+    Workload("bf16_s2_n72", S=2, W=2, n_chunk=10, F=3, Hh=4, Ww=6, n_heads=2,
+             head_dim=128, n_layers=1),
+    # head_dim 64, no anchor, explicit store window
+    Workload("bf16_d64_noanchor", S=3, W=1, W_store=2, anchor=0, n_chunk=9, F=2, Hh=10,
+             Ww=10, n_heads=2, head_dim=64, n_layers=1),
+    # Rolling-Forcing comparison mask
+    Workload("bf16_rolling", S=3, W=2, n_chunk=8, F=2, Hh=8, Ww=15, n_heads=2,
+             head_dim=128, n_layers=1, mask=wf.WF_MASK_ROLLING),
+    # per-head query scale U(0.5, 2)
+    Workload("bf16_headscale", S=2, W=3, n_chunk=9, F=1, Hh=16, Ww=16, n_heads=4,
+             head_dim=128, n_layers=1, q_head_scale=True),
+    # degenerate: one step, no history, no anchor
+    Workload("bf16_s1_w0", S=1, W=0, anchor=0, n_chunk=5, F=1, Hh=8, Ww=8, n_heads=1,
+             head_dim=128, n_layers=1),
+    # degenerate: a single chunk never fills the pipeline
+    Workload("bf16_single_chunk", S=3, W=2, n_chunk=1, F=1, Hh=8, Ww=16, n_heads=2,
+             head_dim=128, n_layers=1),
+]
+
+
+@pytest.mark.parametrize("w", SMALL_BF16, ids=lambda w: w.name)
+def test_small_bf16_every_round(w):
+    _log(f"{w.name}: {w.n_chunk + w.S} rounds")
+    full_rollout(w)
+
+
+@pytest.mark.timeout(600)
+def test_full_size_wan13b_4step_sampled():
+    """1.3B shape, 4 steps, 30 layers: fill (k=4) and steady state with the
+    anchor re-rotated (k=14); first and last layer; 64 sampled rows per
+    (group, head) plus the last row; whole pages."""
+    w = WAN13B_4STEP
+    ro = Rollout(w)
+    try:
+        for k in range(15):
+            _log(f"{w.name} round {k}")
+            ro.run(k)
+            if k in (4, 14):
+                for layer in (0, w.n_layers - 1):
+                    check_publish(ro, k, layer)
+                    err = check_attention(ro, k, layer, rows=64)
+                    _log(f"  k={k} layer={layer} max abs err {err:.3e}")
+    finally:
+        ro.close()
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("w", [WAN13B_5STEP, WAN13B_5STEP_ROLLING], ids=lambda w: w.name)
+def test_full_size_wan13b_5step_sampled(w):
+    ro = Rollout(w)
+    try:
+        for k in range(18):
+            _log(f"{w.name} round {k}")
+            ro.run(k)
+        for layer in (0, w.n_layers - 1):
+            err = check_attention(ro, 17, layer, rows=64)
+            _log(f"  k=17 layer={layer} max abs err {err:.3e}")
+    finally:
+        ro.close()
+
+
+@pytest.mark.timeout(1200)
+def test_full_size_wan14b_4step_sampled():
+    w = WAN14B_4STEP
+    ro = Rollout(w)
+    try:
+        for k in range(15):
+            _log(f"{w.name} round {k}")
+            ro.run(k)
+        err = check_attention(ro, 14, w.n_layers - 1, rows=32)
+        _log(f"  k=14 layer={w.n_layers - 1} max abs err {err:.3e}")
+    finally:
+        ro.close()

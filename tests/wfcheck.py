@@ -1,0 +1,165 @@
+"""Shared helpers of the GPU parity tests: run rounds through the C ABI and
+compare what they produced with the oracle (fp64, CPU).
+
+Inputs come from ``chunk_causal_dit_round_amd.synth`` (seeded, one seed per
+(round, layer, stage, tensor) slice).  The oracle never sees anything the HIP
+path produced: its ``raw`` callback regenerates input slices from their seeds.
+"""
+
+import math
+
+import numpy as np
+import torch
+
+from chunk_causal_dit_round_amd import synth, wf
+from chunk_causal_dit_round_amd.session import Session
+from oracle import wf_plan as P
+from oracle import wf_round as WR
+from oracle.wf_rope import rope3d
+
+# bf16 RNE keeps 8 significant bits: one unit in the last place is at most
+# 2^-7 of the value.  A page value may differ from RNE(exact) by one ulp when
+# the fp32 rotation lands next to a rounding tie.
+BF16_RTOL = 2.0 ** -7
+ATT_TOL = {wf.WF_BF16: 2e-2, wf.WF_F32: 1e-4}
+
+
+def oracle_cfg(w):
+    return P.Config(S=w.S, W=w.W, W_store=w.W_store, anchor=w.anchor, n_chunk=w.n_chunk,
+                    F=w.F, Hh=w.Hh, Ww=w.Ww, n_heads=w.n_heads, head_dim=w.head_dim,
+                    n_layers=w.n_layers, mask=w.mask)
+
+
+class Rollout:
+    """One request of workload ``w`` on the GPU, round by round."""
+
+    def __init__(self, w, device="cuda", gen_device=None, tag=None, perturb=None):
+        self.w = w
+        self.tag = tag or w.name
+        self.sess = Session(w.config(), device=device)
+        self.gen_device = gen_device or ("cpu" if w.n_tokens * w.n_heads * w.head_dim < 1 << 20
+                                         else device)
+        self.q_scale = synth.head_scales(w.n_heads, self.tag) if w.q_head_scale else None
+        self.perturb = perturb or {}      # (round, layer, stage, name) -> additive offset
+        self._raw_cache = {}
+
+    # ---- inputs ----
+    def input_slice(self, rnd, layer, stage, name):
+        s = self.sess
+        x = synth.slice_input(self.tag, rnd, layer, stage, name, s.N, s.H, s.D,
+                              self.gen_device, s.dtype, self.q_scale)
+        off = self.perturb.get((rnd, layer, stage, name))
+        if off is not None:
+            x = (x.float() + off).to(s.dtype)
+        return x
+
+    def fill(self, k):
+        b = self.sess.bufs
+        for layer in range(self.w.n_layers):
+            for s in range(self.w.S + 1):
+                for name in synth.NAMES:
+                    b[name][layer, s].copy_(self.input_slice(k, layer, s, name))
+
+    def raw(self, rnd, layer, stage, name):
+        """Oracle input callback: fp64 copy of a regenerated slice."""
+        key = (rnd, layer, stage, name)
+        if key not in self._raw_cache:
+            if len(self._raw_cache) > 64:
+                self._raw_cache.clear()
+            self._raw_cache[key] = self.input_slice(rnd, layer, stage, name).to(
+                torch.float64).cpu().numpy()
+        return self._raw_cache[key]
+
+    # ---- rounds ----
+    def run(self, k, mode="round", stream=None):
+        s = self.sess
+        assert s.next_round() == k
+        self.fill(k)
+        plan = s.plan(k)
+        if mode == "round":
+            s.run_round(plan, stream=stream)
+        elif mode == "layers":
+            for layer in range(self.w.n_layers):
+                s.publish(plan, layer, stream=stream)
+                s.attention(plan, layer, stream=stream)
+            s.commit(plan)
+        elif mode == "publish_all_first":
+            for layer in range(self.w.n_layers):
+                s.publish(plan, layer, stream=stream)
+            for layer in reversed(range(self.w.n_layers)):
+                s.attention(plan, layer, stream=stream)
+            s.commit(plan)
+        else:
+            raise ValueError(mode)
+        return plan
+
+    def close(self):
+        self.sess.close()
+
+
+def to64(t):
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+def check_publish(ro, k, layer, rows=None):
+    """q_rot and every page the round wrote vs oracle RoPE of the inputs."""
+    w, s = ro.w, ro.sess
+    oc = oracle_cfg(w)
+    torch.cuda.synchronize()
+    exact = s.dtype == torch.float32
+    sel = slice(None) if rows is None else torch.as_tensor(rows)
+    for st in range(w.S + 1):
+        i = k - st
+        if not P.chunk_active(oc, i):
+            continue
+        qr = rope3d(ro.raw(k, layer, st, "q"), w.F * i, w.F, w.Hh, w.Ww)
+        got = to64(s.bufs["q_rot"][layer, st])
+        _close_rope(got[sel], qr[sel], exact, f"q_rot k={k} l={layer} s={st}")
+        slot = P.cell_slot(oc, k, st)
+        K, Vt = s.page(layer, slot)
+        kr = rope3d(ro.raw(k, layer, st, "k"), w.F * i, w.F, w.Hh, w.Ww)
+        _close_rope(to64(K).transpose(1, 0, 2)[sel], kr[sel], exact, f"K k={k} l={layer} s={st}")
+        np.testing.assert_array_equal(to64(Vt).transpose(2, 0, 1), ro.raw(k, layer, st, "v"))
+    if P.anchor_present(oc, k):
+        K, Vt = s.page(layer, P.anchor_slot(oc, k))
+        kr = rope3d(ro.raw(w.S, layer, w.S, "k"), P.anchor_frame0(oc, k), w.F, w.Hh, w.Ww)
+        _close_rope(to64(K).transpose(1, 0, 2), kr, exact, f"anchor K k={k} l={layer}")
+        np.testing.assert_array_equal(to64(Vt).transpose(2, 0, 1), ro.raw(w.S, layer, w.S, "v"))
+
+
+def _close_rope(got, want, exact, what):
+    err = np.abs(got - want)
+    if exact:
+        lim = 2e-6 * (1 + np.abs(want))
+    else:
+        lim = BF16_RTOL * np.abs(want) + 1e-6
+    bad = err > lim
+    assert not bad.any(), f"{what}: {bad.sum()} elements off, max err {err.max():.3e}"
+
+
+def check_attention(ro, k, layer, rows=None, heads=None, stages=None, seed=0):
+    """Attention output vs the oracle; all rows, or ``rows`` random rows per group."""
+    w, s = ro.w, ro.sess
+    oc = oracle_cfg(w)
+    torch.cuda.synchronize()
+    tol = ATT_TOL[w.dtype]
+    worst = 0.0
+    rng = np.random.default_rng([seed, k, layer])
+    for st in (range(w.S + 1) if stages is None else stages):
+        if not P.chunk_active(oc, k - st):
+            continue
+        r = None
+        if rows is not None:
+            r = np.sort(rng.choice(s.N, size=min(rows, s.N), replace=False))
+            r[-1] = s.N - 1           # always include the ragged tail row
+        want = WR.group_output(oc, k, st, layer, ro.raw, rows=r, heads=heads)
+        got = to64(s.bufs["out"][layer, st])
+        if r is not None:
+            got = got[r]
+        if heads is not None:
+            got = got[:, list(heads), :]
+        assert np.isfinite(got).all()
+        err = np.abs(got - want).max()
+        worst = max(worst, err)
+        assert err <= tol, f"attention k={k} l={layer} s={st}: max abs err {err:.3e} > {tol}"
+    return worst
