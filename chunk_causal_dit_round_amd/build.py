@@ -19,6 +19,9 @@ LIB = os.path.join(PKG, "libwf.so")
 ARCH = "gfx950"
 
 HIP_SOURCES = ["wf_runtime.cpp", "wf_publish.hip", "wf_attention.hip"]
+# Attention scores are finite or -inf, never NaN: without NaN semantics the
+# row max needs no canonicalising v_max x,x per score.
+FILE_FLAGS = {"wf_attention.hip": ["-fno-honor-nans"]}
 CXX_SOURCES = ["wf_plan.cpp"]
 
 # Packed fp32 VALU forms are switched off for all device code.
@@ -57,7 +60,7 @@ def build_library(verbose: bool = False) -> str:
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
-        _run([hipcc, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, *lang,
+        _run([hipcc, *HIP_FLAGS, *FILE_FLAGS.get(src, []), "-I", INCLUDE, "-I", CSRC, *lang,
               "-c", os.path.join(CSRC, src), "-o", obj], verbose)
         objs.append(obj)
     tmp = LIB + ".tmp"

@@ -33,6 +33,8 @@
 // query, 32-key LDS tiles, fp32 FMA), used for fp32 rounds.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "wf_kernels.h"
 
 namespace wf {
@@ -40,6 +42,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -53,8 +56,15 @@ __device__ inline int find_group(const AttnArgs& a, int item) {
 // A-operand row order for the QK MFMA: swaps bits 2 and 3.
 __device__ inline int perm_row(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
-// K tile swizzle: distinct for the 8 rows one 8-lane group reads.
-__device__ inline int kswz(int r) { return (r & 3) | ((r >> 1) & 4); }
+// Chunk swizzles of the LDS tiles (16-byte chunk index XOR f(row)).  The
+// MFMA operand reads of lanes 0..15 touch K rows pi(0..15) and Vt rows
+// 0..15 at one logical chunk; both swizzles make every aligned group of 8
+// lanes hit 8 distinct chunks modulo 8 and every group of 16 lanes hit 16
+// distinct 16-byte bank groups, so the reads are conflict-free for either
+// bank width.
+template <int KCH>
+__device__ inline int kswz(int r) { return perm_row(r & 15) & (KCH - 1); }
+__device__ inline int vswz(int d) { return (d & 7) ^ ((d >> 3) & 1); }
 
 // v_permlane32_swap exchanges the upper half of its first operand with the
 // lower half of its second.  With both operands = x the two results hold, in
@@ -70,19 +80,33 @@ __device__ inline float pair_sum32(float x) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void wf_attention_bf16_kernel(const AttnArgs a) {
-  constexpr int BM = kAttnBM_bf16;  // 128 query rows per work-group
+__global__ __launch_bounds__(512, 1) void wf_attention_bf16_kernel(const AttnArgs a) {
+  constexpr int BM = kAttnBM_bf16;  // 256 query rows per work-group
   constexpr int BN = 64;            // keys per tile
+  constexpr int NT = 512;           // threads: 8 waves in two groups of 4
   constexpr int KSTEPS = D / 16;    // MFMA k-steps of QK^T
   constexpr int DT = D / 32;        // 32-row output tiles of O^T
   constexpr int KCH = D / 8;        // 16-byte chunks per K row
   constexpr int VCH = BN / 8;       // 16-byte chunks per Vt row
-  constexpr int TILE = BN * D;      // elements of one K (or Vt) tile
-  constexpr int KLOADS = BN * KCH / 256;
-  constexpr int VLOADS = D * VCH / 256;
-  static_assert(KCH >= 8 && KLOADS * 256 == BN * KCH && VLOADS * 256 == D * VCH, "shape");
+  // LDS rows are padded by one 16-byte chunk: K row r at r * KPITCH, Vt row
+  // d at d * VPITCH (elements).  Lanes 0..15 of an operand read hit 16
+  // different 16-byte bank groups, and a fragment's address is one base
+  // register plus an immediate per k-step.
+  constexpr int KPITCH = D + 8;
+  constexpr int VPITCH = BN + 8;
+  constexpr int KTILE = BN * KPITCH;  // elements of one padded K tile
+  constexpr int VTILE = D * VPITCH;   // elements of one padded Vt tile
+  constexpr int STAGES = 4;         // LDS ring of K+Vt tiles
+  constexpr int KLOADS = BN * KCH / NT;
+  constexpr int VLOADS = D * VCH / NT;
+  constexpr int KROWS = NT / KCH;   // K rows covered by one load round
+  constexpr int VROWS = NT / VCH;   // Vt rows covered by one load round
+  constexpr int NPV = 4 * DT;       // PV MFMAs per tile
+  constexpr int NQK = 2 * KSTEPS;   // QK MFMAs per tile
+  constexpr float kRescale = 8.f;   // lazy rescale threshold (log2 units)
+  static_assert(KCH >= 8 && KLOADS * NT == BN * KCH && VLOADS * NT == D * VCH, "shape");
 
-  __shared__ __attribute__((aligned(16))) __bf16 lds[2][2 * TILE];
+  __shared__ __attribute__((aligned(16))) __bf16 lds[STAGES][KTILE + VTILE];
 
   const int item = blockIdx.x;
   if (item >= a.n_items) return;
@@ -95,11 +119,20 @@ __global__ __launch_bounds__(256, 2) void wf_attention_bf16_kernel(const AttnArg
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int col = lane & 31, half = lane >> 5;
+  const int pgroup = wave >> 2;     // ping-pong group
+  const int n_pages = G.n_pages;
 
-  const __bf16* pool = static_cast<const __bf16*>(a.pool);
-  const int64_t hnd = static_cast<int64_t>(H) * N * D;
-  const int64_t total = static_cast<int64_t>(G.n_pages) * N;
-  const int n_tiles = static_cast<int>((total + BN - 1) / BN);
+  // Byte offsets inside this layer's pool fit in 32 bits (checked on the
+  // host), so every load is "uniform base + 32-bit lane offset".
+  const char* pool = static_cast<const char*>(a.pool);
+  const uint32_t page_bytes = static_cast<uint32_t>(a.page_elems) * 2u;
+  const uint32_t v_part = static_cast<uint32_t>(H) * N * D * 2u;   // Vt after K
+  const uint32_t k_head = static_cast<uint32_t>(h) * N * D * 2u;
+  const uint32_t v_head = v_part + static_cast<uint32_t>(h) * D * N * 2u;
+  const int total = n_pages * N;
+  const int n_full = total / BN;
+  const int tail = total - n_full * BN;
+  const int n_tiles = n_full + (tail > 0 ? 1 : 0);
 
   // Query fragments (B operand of S^T = K Q^T): lane holds query `col`,
   // dims 16 s + 8 half .. +7.  Rows past N are clamped (never stored).
@@ -111,144 +144,222 @@ __global__ __launch_bounds__(256, 2) void wf_attention_bf16_kernel(const AttnArg
 #pragma unroll
   for (int s = 0; s < KSTEPS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * half);
 
-  // Per-thread load assignment.
-  const int kc = tid % KCH, kr0 = tid / KCH;        // K: chunk, first row
-  const int vc = tid % VCH, vd0 = tid / VCH;        // Vt: key chunk, first dim
-  u32x4 kreg[KLOADS], vreg[VLOADS];
+  // Per-thread load assignment: K rows kr0 + i*KROWS, chunk kc; Vt rows
+  // (value dims) vd0 + i*VROWS, keys 8*vc .. 8*vc+7 of the tile.
+  const int kc = tid % KCH, kr0 = tid / KCH;
+  const int vc = tid % VCH, vd0 = tid / VCH;
+  uint32_t tk[KLOADS], tv[VLOADS];
+#pragma unroll
+  for (int i = 0; i < KLOADS; ++i) tk[i] = static_cast<uint32_t>(((kr0 + i * KROWS) * D + kc * 8) * 2);
+#pragma unroll
+  for (int i = 0; i < VLOADS; ++i) tv[i] = static_cast<uint32_t>(((vd0 + i * VROWS) * N + vc * 8) * 2);
 
-  auto load_tile = [&](int t) {
-    const int64_t key0 = static_cast<int64_t>(t) * BN;
-    const int p0 = static_cast<int>(key0 / N);
-    const int64_t bound = static_cast<int64_t>(p0 + 1) * N;
+  // LDS byte addresses (within a stage) of this lane's MFMA operands: K row
+  // pi(col), dims 8 half ..; Vt row col, keys 8 half ..
+  const uint32_t ka = static_cast<uint32_t>((perm_row(col) * KPITCH + 8 * half) * 2);
+  const uint32_t va = static_cast<uint32_t>((KTILE + col * VPITCH + 8 * half) * 2);
+  const char* lds_bytes = reinterpret_cast<const char*>(&lds[0][0]);
+  constexpr uint32_t kStageBytes = (KTILE + VTILE) * 2;
+
+  u32x4 kreg[KLOADS], vreg[VLOADS];
+  // Byte offset of every context page's slot, one page per lane; tile loads
+  // read the two they need with v_readlane (uniform page index).
+  const uint32_t lane_slot = lane < n_pages ? static_cast<uint32_t>(G.slot[lane]) * page_bytes : 0u;
+  // Page and row of the next tile to load (a 64-key tile straddles at most
+  // one page boundary, so the position advances without division).
+  int lp = 0, lrow = 0, lnext = 0;
+
+  // Global -> registers for tile `lnext`.  The partial last tile clamps its
+  // keys past the end of the context to the tile's first key (finite data;
+  // their scores are masked).
+  auto load_tile = [&](auto last_c) {
+    constexpr bool last = decltype(last_c)::value;
+    const int p1 = lp + 1 < n_pages ? lp + 1 : lp;
+    const uint32_t s0 = __builtin_amdgcn_readlane(lane_slot, lp);
+    const uint32_t s1 = __builtin_amdgcn_readlane(lane_slot, p1);
+    const int left = N - lrow;            // keys of the tile still in page lp
+    const uint32_t kb0 = s0 + k_head + static_cast<uint32_t>(lrow * D * 2);
+    const uint32_t kb1 = s1 + k_head + static_cast<uint32_t>((lrow - N) * D * 2);
 #pragma unroll
     for (int i = 0; i < KLOADS; ++i) {
-      const int r = kr0 + i * (256 / KCH);
-      const int64_t key = key0 + r;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (key < total) {
-        const int p = key < bound ? p0 : p0 + 1;
-        const int64_t row = key - static_cast<int64_t>(p) * N;
-        const __bf16* src = pool + static_cast<int64_t>(G.slot[p]) * a.page_elems +
-                            (static_cast<int64_t>(h) * N + row) * D + kc * 8;
-        x = *reinterpret_cast<const u32x4*>(src);
-      }
-      kreg[i] = x;
+      const int r = kr0 + i * KROWS;
+      uint32_t off = (r < left ? kb0 : kb1) + tk[i];
+      if (last && r >= tail) off = kb0 + static_cast<uint32_t>(kc * 16);
+      kreg[i] = *reinterpret_cast<const u32x4*>(pool + off);
     }
-    // 8 keys of one Vt chunk never straddle a page (N % 8 == 0).
-    const int64_t vkey = key0 + vc * 8;
-    const bool vok = vkey < total;
-    const int vp = vkey < bound ? p0 : p0 + 1;
-    const int64_t vrow = vkey - static_cast<int64_t>(vp) * N;
-    const __bf16* vbase = pool + static_cast<int64_t>(vok ? G.slot[vp] : 0) * a.page_elems + hnd +
-                          static_cast<int64_t>(h) * D * N + vrow;
+    const uint32_t vb0 = s0 + v_head + static_cast<uint32_t>(lrow * 2);
+    const uint32_t vb1 = s1 + v_head + static_cast<uint32_t>((lrow - N) * 2);
+    const uint32_t vbase = 8 * vc < left ? vb0 : vb1;
+    const bool vclamp = last && 8 * vc >= tail;
 #pragma unroll
     for (int i = 0; i < VLOADS; ++i) {
-      const int d = vd0 + i * (256 / VCH);
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (vok) x = *reinterpret_cast<const u32x4*>(vbase + static_cast<int64_t>(d) * N);
-      vreg[i] = x;
+      const uint32_t off = vclamp ? vb0 + static_cast<uint32_t>((vd0 + i * VROWS) * N * 2) : vbase + tv[i];
+      vreg[i] = *reinterpret_cast<const u32x4*>(pool + off);
     }
+    lrow += BN;
+    if (lrow >= N) {
+      lrow -= N;
+      ++lp;
+    }
+    ++lnext;
   };
-  auto store_tile = [&](int buf) {
-    __bf16* kt = lds[buf];
-    __bf16* vt = lds[buf] + TILE;
+  auto load_next = [&]() {
+    if (lnext == n_full) load_tile(std::true_type{});
+    else load_tile(std::false_type{});
+  };
+  auto store_tile = [&](int stage) {
+    __bf16* kt = lds[stage];
+    __bf16* vt = lds[stage] + KTILE;
 #pragma unroll
-    for (int i = 0; i < KLOADS; ++i) {
-      const int r = kr0 + i * (256 / KCH);
-      *reinterpret_cast<u32x4*>(kt + r * D + ((kc ^ kswz(r)) * 8)) = kreg[i];
-    }
+    for (int i = 0; i < KLOADS; ++i)
+      *reinterpret_cast<u32x4*>(kt + (kr0 + i * KROWS) * KPITCH + kc * 8) = kreg[i];
 #pragma unroll
-    for (int i = 0; i < VLOADS; ++i) {
-      const int d = vd0 + i * (256 / VCH);
-      *reinterpret_cast<u32x4*>(vt + d * BN + ((vc ^ (d & 7)) * 8)) = vreg[i];
-    }
+    for (int i = 0; i < VLOADS; ++i)
+      *reinterpret_cast<u32x4*>(vt + (vd0 + i * VROWS) * VPITCH + vc * 8) = vreg[i];
   };
 
   f32x16 oacc[DT];
 #pragma unroll
   for (int i = 0; i < DT; ++i) oacc[i] = f32x16{};
+  f32x16 sacc[2];
+  bf16x8 pf[2][2];
   float m_run = -__builtin_inff();
   float l_run = 0.f;
   const float c = a.scale_log2e;
+  const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < n_tiles) load_tile(t + 1);
-    const __bf16* kt = lds[buf];
-    const __bf16* vt = lds[buf] + TILE;
-
-    // ---- S^T = K Q^T for 64 keys (two 32-key MFMA tiles) ----
-    f32x16 sacc[2];
+  // ---- MFMA cluster: O^T += Vt(t-1) P(t-1)^T, then S^T(t) = K(t) Q^T.
+  // Operand fragments are read from LDS kAhead MFMAs ahead; the scheduling
+  // barriers pin that order (the register allocator would otherwise read
+  // each fragment right before its MFMA and expose the LDS latency).
+  constexpr int kAhead = 4;
+  auto mfma_cluster = [&](int pv_stage, int qk_stage) {
+    const char* vbase = lds_bytes + pv_stage * kStageBytes;
+    const char* kbase = lds_bytes + qk_stage * kStageBytes;
+    auto frag = [&](int i) -> bf16x8 {
+      if (i < NPV) {
+        const int kk = i / DT, dt = i % DT;
+        return *reinterpret_cast<const bf16x8*>(vbase + va + (dt * 32 * VPITCH + kk * 16) * 2);
+      }
+      const int j = i - NPV, s = j >> 1, t2 = j & 1;
+      return *reinterpret_cast<const bf16x8*>(kbase + ka + (t2 * 32 * KPITCH + s * 16) * 2);
+    };
+    constexpr int NI = NPV + NQK;
+    bf16x8 fr[kAhead + 1];
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
-      sacc[t2] = f32x16{};
-      const int r = 32 * t2 + perm_row(col);
+    for (int i = 0; i < kAhead; ++i) fr[i] = frag(i);
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
-        const int ch = 2 * s + half;
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kt + r * D + ((ch ^ kswz(r)) * 8));
-        sacc[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[t2], 0, 0, 0);
+    for (int i = 0; i < NI; ++i) {
+      if (i + kAhead < NI) fr[(i + kAhead) % (kAhead + 1)] = frag(i + kAhead);
+      const bf16x8 f = fr[i % (kAhead + 1)];
+      if (i < NPV) {
+        const int kk = i / DT, dt = i % DT;
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, pf[kk >> 1][kk & 1], oacc[dt], 0, 0, 0);
+      } else {
+        const int j = i - NPV, s = j >> 1, t2 = j & 1;
+        sacc[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qf[s], s == 0 ? f32x16{} : sacc[t2], 0, 0, 0);
       }
     }
+    // order: kAhead LDS reads, then (MFMA, LDS read) pairs, then MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i + kAhead < NI) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
 
-    // ---- online softmax (base 2); value v of tile t2 is key
-    //      32 t2 + 16 (v / 8) + 8 half + (v % 8) ----
-    const int64_t kbase = static_cast<int64_t>(t) * BN;
-    if (kbase + BN > total) {
+  // ---- VALU cluster: online softmax of S(t) (base 2, lazy rescale) ----
+  auto softmax = [&](int valid) {
+    // value v of tile t2 is key 32 t2 + 16 (v / 8) + 8 half + (v % 8)
+    if (valid < BN) {
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int64_t key = kbase + 32 * t2 + 16 * (v >> 3) + 8 * half + (v & 7);
-          if (key >= total) sacc[t2][v] = -__builtin_inff();
-        }
+        for (int v = 0; v < 16; ++v)
+          if (32 * t2 + 16 * (v >> 3) + 8 * half + (v & 7) >= valid) sacc[t2][v] = -__builtin_inff();
     }
-    float mx = sacc[0][0];
+    float mx = fmaxf(sacc[0][0], sacc[1][0]);
 #pragma unroll
-    for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sacc[0][v]);
+    for (int v = 1; v < 16; ++v) mx = fmaxf(mx, fmaxf(sacc[0][v], sacc[1][v]));
+    mx = pair_max32(mx) * c;
+    if (__any(mx > m_run + kRescale)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[1][v]);
-    mx = pair_max32(mx);
-    const float m_new = fmaxf(m_run, mx * c);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    float ls = 0.f;
-    bf16x8 pf[2][2];
+      for (int i = 0; i < DT; ++i) oacc[i] *= alpha;
+    }
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t2][v], c, -m_new));
-        ls += p;
-        pf[t2][v >> 3][v & 7] = static_cast<__bf16>(p);
-      }
-    l_run = l_run * alpha + ls;
+      for (int v = 0; v < 16; ++v)
+        pf[t2][v >> 3][v & 7] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t2][v], c, -m_run)));
+    // row sum of the rounded P (exactly what the PV product uses)
 #pragma unroll
-    for (int i = 0; i < DT; ++i) oacc[i] *= alpha;
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int a2 = 0; a2 < 2; ++a2)
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const bf16x2 pp = {pf[t2][a2][e], pf[t2][a2][e + 1]};
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_run, false);
+        }
+  };
 
-    // ---- O^T += Vt P^T ----
+  // ---- prologue: tiles 0..2 into stages 0..2.  The first MFMA cluster
+  // multiplies P = 0 with the Vt region of the last stage, which is zeroed
+  // so that stale LDS contents cannot turn 0 * x into NaN. ----
+  const int pre = n_tiles < STAGES - 1 ? n_tiles : STAGES - 1;
+  for (int t = 0; t < pre; ++t) {
+    load_next();
+    store_tile(t);
+  }
+  {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    __bf16* vz = lds[STAGES - 1] + KTILE;
+    for (int i = tid; i < VTILE / 8; i += NT) *reinterpret_cast<u32x4*>(vz + i * 8) = z;
+  }
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int d = 32 * dt + col;
+  for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int ch = 2 * kk + half;
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vt + d * BN + ((ch ^ (d & 7)) * 8));
-        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kk >> 1][kk & 1], oacc[dt], 0, 0, 0);
+    for (int a2 = 0; a2 < 2; ++a2)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf[t2][a2][e] = static_cast<__bf16>(0.f);
+  __syncthreads();
+
+  // Ping-pong: the two wave groups run the same sequence of clusters one
+  // cluster apart (group 1 first passes one extra barrier), so on every SIMD
+  // one wave issues MFMAs while the other runs the softmax.  Every cluster
+  // ends at a work-group barrier; both groups pass the same number.  The
+  // last MFMA cluster's S^T is not used.
+  // Nothing from before the loop (query fragments, prologue tiles) is in
+  // flight any more; saying so keeps the loop's only vector-memory waits on
+  // the staged tile loads, where their data is consumed.
+  __builtin_amdgcn_s_waitcnt(0);
+  if (pgroup == 1) __syncthreads();
+  bool staged = false;
+  for (int t = 0; t <= n_tiles; ++t) {
+    mfma_cluster((t - 1) & (STAGES - 1), t & (STAGES - 1));
+    __syncthreads();
+    if (t < n_tiles) {
+      // tile t+2 was fetched into registers one tile ago; its stage last
+      // held tile t-2, whose final reader ran two clusters ago.
+      if (staged) store_tile((t + 2) & (STAGES - 1));
+      staged = false;
+      if (t + 3 < n_tiles) {
+        load_next();
+        staged = true;
       }
+      softmax(t < n_full ? BN : tail);
     }
-
-    if (t + 1 < n_tiles) store_tile(buf ^ 1);
     __syncthreads();
   }
+  if (pgroup == 0) __syncthreads();
 
-  // ---- epilogue: O = O^T^T / l ----
-  const float l_tot = pair_sum32(l_run);
-  const float inv = 1.f / l_tot;
+  // ---- epilogue: O = (O^T)^T / l ----
+  const float inv = 1.f / pair_sum32(l_run);
   if (q < N) {
     __bf16* orow = static_cast<__bf16*>(a.out) +
                    ((static_cast<int64_t>(G.stage) * N + q) * H + h) * D;
@@ -382,9 +493,9 @@ hipError_t launch_attention(const AttnArgs& a, int dtype, hipStream_t stream) {
   const dim3 grid(a.n_items);
   if (dtype == WF_BF16) {
     if (a.D == 128) {
-      hipLaunchKernelGGL(wf_attention_bf16_kernel<128>, grid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL(wf_attention_bf16_kernel<128>, grid, dim3(512), 0, stream, a);
     } else if (a.D == 64) {
-      hipLaunchKernelGGL(wf_attention_bf16_kernel<64>, grid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL(wf_attention_bf16_kernel<64>, grid, dim3(512), 0, stream, a);
     } else {
       return hipErrorInvalidValue;
     }

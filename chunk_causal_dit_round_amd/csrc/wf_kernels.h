@@ -64,7 +64,7 @@ struct AttnArgs {
 };
 
 // Query rows per work item of each attention instance.
-constexpr int kAttnBM_bf16 = 128;
+constexpr int kAttnBM_bf16 = 256;
 constexpr int kAttnBM_f32 = 64;
 
 hipError_t launch_publish(const PublishArgs& a, int dtype, hipStream_t stream);

@@ -49,6 +49,9 @@ wf_status check_supported(const wf::Shape& sh) {
     if (sh.N % 8 != 0) return fail(WF_EUNSUPPORTED, "bf16 kernels need tokens per chunk % 8 == 0");
     // A 64-key tile then straddles at most one page boundary.
     if (sh.N < 64) return fail(WF_EUNSUPPORTED, "bf16 kernels need tokens per chunk >= 64");
+    // Attention addresses a layer's slots with 32-bit byte offsets.
+    if (double(sh.n_slots) * double(sh.page_elems) * 2.0 >= 4294967296.0)
+      return fail(WF_EUNSUPPORTED, "bf16 kernels need one layer's slot pool below 4 GiB");
   } else {
     if (sh.D % 4 != 0 || sh.D > 128)
       return fail(WF_EUNSUPPORTED, "fp32 kernels need head_dim % 4 == 0 and <= 128");

@@ -175,7 +175,8 @@ wf_status wf_pool_bytes(const wf_config* cfg, size_t* pool_bytes,
 /* Attach caller-owned device buffers and upload the RoPE tables (computed
  * on the host in fp64, stored as fp32) with a synchronous copy.  Sizes are
  * checked first (WF_ESMALL), then kernel support for the config
- * (WF_EUNSUPPORTED: bf16 needs head_dim 64 or 128, N % 8 == 0, N >= 64; fp32
+ * (WF_EUNSUPPORTED: bf16 needs head_dim 64 or 128, N % 8 == 0, N >= 64 and
+ * one layer's slots below 4 GiB; fp32
  * needs head_dim % 4 == 0, head_dim <= 128 and N % 4 == 0).  Buffers must
  * be 16-byte aligned.  The handle keeps the pointers, not the memory. */
 wf_status wf_bind(wf_handle* h, void* d_pool, size_t pool_bytes,
