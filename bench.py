@@ -13,11 +13,20 @@ round).  `roofline` is the attention kernel's: algorithmic FLOPs per launch
 (readable key tokens only) / its mean duration from HIP events recorded on
 the launch stream around every attention launch in the timed region.
 `cpu_baseline` is the fp64 oracle on a bounded sample, timed on this host.
+
+Other modes (one JSON line each):
+  --rollout          the whole long request (133 chunks, 137 rounds) with fresh
+                     per-round inputs (generated between rounds, untimed): steady,
+                     full-width and whole-request rounds/s.
+  --copy-calibration a plain device copy of known size, for scaling the HBM
+                     FETCH_SIZE / WRITE_SIZE counters to bytes.
 """
 
 import argparse
+import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -26,6 +35,21 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0
+ATTN_SRC = os.path.join(ROOT, "chunk_causal_dit_round_amd", "csrc", "wf_attention.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_bf16_wan1.3b_4step_hbm_traffic.txt")
+
+
+def measured_traffic():
+    """HBM bytes per attention launch from the committed counter summary, or
+    None if the kernel source changed since the counters were taken."""
+    try:
+        fields = dict(line.split(":", 1) for line in open(TRAFFIC_FILE) if ":" in line)
+        src = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+        if fields.get("kernel_source_sha256", "").strip() != src:
+            return None
+        return float(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def parse():
@@ -37,7 +61,63 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=1,
                     help="heads of one layer the oracle baseline times")
+    ap.add_argument("--rollout", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain device copy of 2 GiB, five times (read 2 GiB + write 2 GiB each)."""
+    import torch
+    n = 2 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / 5
+    print(json.dumps({"mode": "copy_calibration", "bytes_read": n, "bytes_written": n,
+                      "ms_per_copy": dt * 1e3, "gbps": 2 * n / dt / 1e9}), flush=True)
+
+
+def rollout(w):
+    """Every round of one request, fresh inputs per round (untimed)."""
+    import torch
+
+    from chunk_causal_dit_round_amd import synth
+    from chunk_causal_dit_round_amd.session import Session
+
+    sess = Session(w.config(), device="cuda")
+    n_rounds = w.n_chunk + w.S
+    w_store = w.W + w.S if w.W_store < 0 else w.W_store
+    k_steady = w.S + max(w.W, w_store) + 1
+    stream = torch.cuda.current_stream()
+    times = []
+    for k in range(n_rounds):
+        synth.fill_round(sess.bufs, "rollout", k, w.n_layers, w.S + 1)
+        plan = sess.plan(k)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        sess.run_round(plan, stream=stream)
+        e1.record(stream)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1) / 1e3)
+        if k % 20 == 0:
+            print(f"# rollout round {k}: {times[-1] * 1e3:.1f} ms", file=sys.stderr, flush=True)
+    steady = times[k_steady:w.n_chunk]
+    full = times[w.S:w.n_chunk]
+    res = {"mode": "rollout", "metric": "wavefront rounds/sec (=chunks/sec)",
+           "workload": f"{w.name} long rollout, {w.n_chunk} chunks, {n_rounds} rounds",
+           "steady_rounds_per_s": 1.0 / statistics.median(steady),
+           "steady_rounds": [k_steady, w.n_chunk - 1],
+           "full_width_rounds_per_s": 1.0 / statistics.median(full),
+           "request_chunks_per_s": w.n_chunk / sum(times),
+           "request_seconds": sum(times),
+           "slowest_round_ms": max(times) * 1e3, "fastest_round_ms": min(times) * 1e3}
+    print(json.dumps(res), flush=True)
 
 
 def oracle_baseline(w, k, layer, heads, raw):
@@ -84,6 +164,12 @@ def main():
     from chunk_causal_dit_round_amd.workloads import ALL
 
     w = ALL[args.workload]
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    if args.rollout:
+        rollout(w)
+        return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     sess = Session(w.config(), device=dev)
@@ -164,7 +250,8 @@ def main():
                    "head_dim": w.head_dim, "layers": L,
                    "rounds_timed": [k0, k0 + args.steps - 1], "n_rounds": n_rounds},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": measured_traffic(),
                      "kernel": "wf_attention_bf16_kernel<128>",
                      "flops_per_launch": flops_launch, "avg_launch_ms": att_avg},
         "attention_tflops_round": total_flops / elapsed / 1e12,

@@ -58,6 +58,10 @@ class WfError(RuntimeError):
 
 
 def _load():
+    # torch ships its own HIP runtime; it must be the one in the process
+    # before libwf.so is loaded, or the library's libamdhip64 dependency binds
+    # the system copy first and torch then finds no usable device.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
     lib = ctypes.CDLL(LIB_PATH)
