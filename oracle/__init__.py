@@ -15,9 +15,11 @@ Modules
 wf_plan       schedule, ordered key-page lists, slot ring (integer work)
 wf_rope       3D rotary position embedding in fp64
 wf_attention  dense softmax attention in fp64
+wf_fp8        FP8 (E4M3) page and query quantisation reading
 wf_round      one round assembled by logical chunk identity (never by slot)
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against printed values, closed forms, invariants or library routines
-(torch CPU ``scaled_dot_product_attention``, complex multiplication).
+(torch CPU ``scaled_dot_product_attention``, complex multiplication,
+torch's ``float8_e4m3fn``).
 """

@@ -26,6 +26,7 @@ import math
 
 import numpy as np
 
+from . import wf_fp8 as F8
 from . import wf_plan as P
 from .wf_attention import attend
 from .wf_rope import rope3d
@@ -49,9 +50,19 @@ def scale_of(cfg: P.Config) -> float:
     return 1.0 / math.sqrt(cfg.head_dim)
 
 
-def group_keys(cfg: P.Config, k: int, stage: int, layer: int, raw, heads=None):
+def _fp8_page(x: np.ndarray) -> np.ndarray:
+    """One page [N, H', d] as FP8 pages hold it: each head quantised per
+    64-token tile (App. C.6 reading in ``wf_fp8``), dequantised."""
+    out = np.empty_like(x)
+    for h in range(x.shape[1]):
+        out[:, h, :] = F8.fp8_tiles(x[:, h, :])
+    return out
+
+
+def group_keys(cfg: P.Config, k: int, stage: int, layer: int, raw, heads=None, fp8=False):
     """Concatenated rotated keys and values of query stage ``stage``:
-    ([N_k, H', d], [N_k, H', d]) in plan order (WF §3.1, Eq. 5)."""
+    ([N_k, H', d], [N_k, H', d]) in plan order (WF §3.1, Eq. 5).  With
+    ``fp8`` each page is the FP8 page of the App. C.6 reading."""
     ks, vs = [], []
     for kind, chunk, _slot in P.key_entries(cfg, k, stage):
         rnd, cell, frame0 = entry_source(cfg, k, kind, chunk)
@@ -59,7 +70,10 @@ def group_keys(cfg: P.Config, k: int, stage: int, layer: int, raw, heads=None):
         vr = np.asarray(raw(rnd, layer, cell, "v"), dtype=np.float64)
         if heads is not None:
             kr, vr = kr[:, heads, :], vr[:, heads, :]
-        ks.append(rope3d(kr, frame0, cfg.F, cfg.Hh, cfg.Ww, cfg.rope_theta))
+        kr = rope3d(kr, frame0, cfg.F, cfg.Hh, cfg.Ww, cfg.rope_theta)
+        if fp8:
+            kr, vr = _fp8_page(kr), _fp8_page(vr)
+        ks.append(kr)
         vs.append(vr)
     return np.concatenate(ks, axis=0), np.concatenate(vs, axis=0)
 
@@ -71,21 +85,26 @@ def q_rot(cfg: P.Config, k: int, stage: int, layer: int, raw) -> np.ndarray:
 
 
 def group_output(cfg: P.Config, k: int, stage: int, layer: int, raw,
-                 rows=None, heads=None) -> np.ndarray:
+                 rows=None, heads=None, fp8=False) -> np.ndarray:
     """Attention output of query stage ``stage``: [len(rows), len(heads), d].
 
     ``rows`` / ``heads`` select query tokens and heads (all by default);
-    every selected row still attends to its full key list.
+    every selected row still attends to its full key list.  With ``fp8`` the
+    pages are FP8 pages and each rotated query row, stored in bf16, is
+    quantised per row (App. C.6 reading in ``wf_fp8``).
     """
     heads = list(range(cfg.n_heads)) if heads is None else list(heads)
     qr = q_rot(cfg, k, stage, layer, raw)
     if rows is not None:
         qr = qr[np.asarray(rows)]
-    kk, vv = group_keys(cfg, k, stage, layer, raw, heads)
+    kk, vv = group_keys(cfg, k, stage, layer, raw, heads, fp8=fp8)
     out = np.empty((qr.shape[0], len(heads), cfg.head_dim), dtype=np.float64)
     sc = scale_of(cfg)
     for hi, h in enumerate(heads):
-        out[:, hi, :] = attend(qr[:, h, :], kk[:, hi, :], vv[:, hi, :], sc)
+        qh = qr[:, h, :]
+        if fp8:
+            qh = F8.fp8_rows(F8.bf16_round(qh))
+        out[:, hi, :] = attend(qh, kk[:, hi, :], vv[:, hi, :], sc)
     return out
 
 
