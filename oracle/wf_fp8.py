@@ -9,7 +9,8 @@ neither the FP8 format nor the scale granularity.  Readings taken here:
 
 * Format: OCP E4M3 -- 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits,
   subnormals below 2^-6, largest finite value 448, no infinities, NaN codes
-  0x7F / 0xFF.  Conversion rounds to nearest, ties to even.
+  0x7F / 0xFF.  Conversion rounds to nearest, ties to even, and keeps the
+  sign of a value that rounds to zero (-0 is 0x80).
 * Scales are powers of two.  A block with largest magnitude ``amax`` uses the
   smallest integer exponent e with amax <= 448 * 2^e (e = 0 for an all-zero
   block), and stores x / 2^e.
@@ -69,7 +70,8 @@ def e4m3_encode(x) -> np.ndarray:
     pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
     code = np.where(pick_hi, hi, lo).astype(np.int64)
     code = np.where(ax == _POS[hi], hi, code)
-    return (code | np.where(np.signbit(x) & (code != 0), 0x80, 0)).astype(np.uint8)
+    # the sign survives rounding to zero (a negative value gives -0, 0x80)
+    return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
 
 
 def e4m3_values(codes) -> np.ndarray:

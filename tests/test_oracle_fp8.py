@@ -58,11 +58,11 @@ def test_encode_matches_torch_rounding_including_ties():
     rng = np.random.default_rng(5)
     rand = rng.uniform(-448, 448, 4000) * 2.0 ** rng.integers(-12, 1, 4000)
     x = np.concatenate([pos, -pos, mids, -mids, quarter, three_q, rand])
+    tiny = np.array([-1e-6, -0.0, 0.0, 1e-6, -2.0 ** -10, -0.00098, 2.0 ** -10])
+    x = np.concatenate([x, tiny])
     ours = F.e4m3_encode(x)
     ref = torch_encode(x)
-    zero = F.e4m3_values(ours) == 0
-    assert np.array_equal(ours[~zero], ref[~zero])
-    assert np.all(torch_decode(ref[zero]) == 0)
+    assert np.array_equal(ours, ref)                     # codes, signed zeros included
 
 
 def test_ties_go_to_even_code():
