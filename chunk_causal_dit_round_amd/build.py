@@ -1,8 +1,7 @@
 """Builds ``libwf.so`` (HIP kernels + C ABI) in-tree for gfx950.
 
 Usage: ``python -m chunk_causal_dit_round_amd.build`` or ``build_library()``.
-Always recompiles.  A host-only variant of the scheduler (``g++`` with
-sanitizers) is built by ``build_host_check()`` for CPU tests.
+Always recompiles.
 """
 
 import os
@@ -18,10 +17,11 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libwf.so")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["wf_runtime.cpp", "wf_publish.hip", "wf_attention.hip"]
+HIP_SOURCES = ["wf_runtime.cpp", "wf_publish.hip", "wf_attention.hip", "wf_attention_fp8.hip"]
 # Attention scores are finite or -inf, never NaN: without NaN semantics the
 # row max needs no canonicalising v_max x,x per score.
-FILE_FLAGS = {"wf_attention.hip": ["-fno-honor-nans", "-Wno-inline-asm"]}
+FILE_FLAGS = {"wf_attention.hip": ["-fno-honor-nans"],
+              "wf_attention_fp8.hip": ["-fno-honor-nans"]}
 CXX_SOURCES = ["wf_plan.cpp"]
 
 # Packed fp32 VALU forms are switched off for all device code.
@@ -67,18 +67,3 @@ def build_library(verbose: bool = False) -> str:
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
-
-
-def build_host_check(verbose: bool = False) -> str:
-    """Host-only scheduler + checker built with ASan/UBSan (no HIP)."""
-    os.makedirs(BUILD, exist_ok=True)
-    exe = os.path.join(BUILD, "plan_check")
-    _run(["g++", "-O1", "-g", "-std=c++17", "-fsanitize=address,undefined",
-          "-fno-sanitize-recover=all", "-Wall", "-I", INCLUDE, "-I", CSRC,
-          os.path.join(CSRC, "wf_plan.cpp"), os.path.join(CSRC, "plan_check.cpp"),
-          "-o", exe], verbose)
-    return exe
-
-
-if __name__ == "__main__":
-    print(build_library(verbose=True))

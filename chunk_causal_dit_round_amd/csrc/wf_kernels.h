@@ -33,9 +33,11 @@ struct PublishArgs {
   void* pool;             // this layer's [n_slots] pages
   void* anchor_raw;       // this layer's anchor page (raw K, Vt)
   const float2* rope;     // [n_frames*nt | Hh*nh | Ww*nw] (cos, sin)
-  int64_t page_elems;     // 2 H N D
+  int64_t page_elems;     // 2 H N D (fp32 / bf16 pages)
+  int64_t page_bytes;     // bytes per pool page (all dtypes)
   int32_t N, H, D, F, Hh, Ww;
   int32_t nt, nh, nw, n_frames;
+  int32_t Npad, T;        // FP8 pages: tokens padded to 64 T, T tiles
   int32_t n_tasks;
   int32_t pad_;
   PublishTask task[WF_MAX_GROUPS + 1];
@@ -53,21 +55,27 @@ struct AttnArgs {
   const void* q_rot;   // [S+1][N][H][D]
   void* out;           // [S+1][N][H][D]
   const void* pool;    // this layer's [n_slots] pages
-  int64_t page_elems;
+  int64_t page_elems;  // fp32 / bf16 pages
+  int64_t page_bytes;  // bytes per pool page (all dtypes)
   int32_t N, H, D;
   float scale_log2e;   // softmax scale * log2(e)
   int32_t n_groups;    // active groups, longest context first
   int32_t q_tiles;     // query tiles per (group, head)
   int32_t n_items;     // sum over groups of H * q_tiles
+  int32_t Npad, T;     // FP8 pages: tokens padded to 64 T, T tiles
   int32_t pad_;
   AttnGroup grp[WF_MAX_GROUPS];
 };
 
 // Query rows per work item of each attention instance.
 constexpr int kAttnBM_bf16 = 256;
+constexpr int kAttnBM_fp8 = 256;
 constexpr int kAttnBM_f32 = 64;
+// FP8 attention keeps the scale codes of a group's whole context in LDS.
+constexpr int kFp8MaxCtxTiles = 4096;
 
 hipError_t launch_publish(const PublishArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_attention(const AttnArgs& a, int dtype, hipStream_t stream);
+hipError_t launch_attention_fp8(const AttnArgs& a, hipStream_t stream);
 
 }  // namespace wf

@@ -35,7 +35,8 @@ bool derive_shape(const wf_config* c, Shape* o, std::string* why) {
   if (c->head_dim < 6 || c->head_dim > 512 || (c->head_dim & 1))
     return fail(why, "head_dim must be even and in [6, 512]");
   if (c->n_layers < 1 || c->n_layers > 4096) return fail(why, "n_layers must be in [1, 4096]");
-  if (c->dtype != WF_F32 && c->dtype != WF_BF16) return fail(why, "dtype must be WF_F32 or WF_BF16");
+  if (c->dtype != WF_F32 && c->dtype != WF_BF16 && c->dtype != WF_FP8)
+    return fail(why, "dtype must be WF_F32, WF_BF16 or WF_FP8");
   if (c->mask != WF_MASK_WAVE && c->mask != WF_MASK_ROLLING)
     return fail(why, "mask must be WF_MASK_WAVE or WF_MASK_ROLLING");
   if (c->reserved != 0) return fail(why, "reserved must be 0");
@@ -72,13 +73,24 @@ bool derive_shape(const wf_config* c, Shape* o, std::string* why) {
   s.mask = c->mask;
   s.theta = c->rope_theta == 0.0 ? 10000.0 : c->rope_theta;
   s.scale = c->softmax_scale == 0.0 ? 1.0 / std::sqrt(double(s.D)) : c->softmax_scale;
-  s.elem = c->dtype == WF_BF16 ? 2 : 4;
+  s.elem = c->dtype == WF_F32 ? 4 : 2;
+  s.T = (s.N + 63) / 64;
+  s.Npad = 64 * s.T;
   size_t pe = 0, tmp = 0;
   if (!mul_ok(size_t(2) * s.H, size_t(s.N), &pe) || !mul_ok(pe, size_t(s.D), &pe))
     return fail(why, "page size overflows");
   s.page_elems = pe;
-  if (!mul_ok(pe, s.elem, &tmp) || !mul_ok(tmp, size_t(s.L) * s.n_slots, &tmp))
-    return fail(why, "pool size overflows");
+  if (!mul_ok(pe, s.elem, &s.anchor_page_bytes)) return fail(why, "page size overflows");
+  if (c->dtype == WF_FP8) {
+    size_t kv = 0;
+    if (!mul_ok(size_t(2) * s.H, size_t(s.Npad), &kv) || !mul_ok(kv, size_t(s.D), &kv))
+      return fail(why, "page size overflows");
+    const size_t codes = size_t(2) * s.H * s.T;
+    s.page_bytes = (kv + codes + 255) / 256 * 256;
+  } else {
+    s.page_bytes = s.anchor_page_bytes;
+  }
+  if (!mul_ok(s.page_bytes, size_t(s.L) * s.n_slots, &tmp)) return fail(why, "pool size overflows");
   *o = s;
   return true;
 }
@@ -100,8 +112,8 @@ uint64_t config_hash(const wf_config& c) {
   return h;
 }
 
-size_t pool_bytes(const Shape& sh) { return size_t(sh.L) * sh.n_slots * sh.page_elems * sh.elem; }
-size_t anchor_bytes(const Shape& sh) { return size_t(sh.L) * sh.page_elems * sh.elem; }
+size_t pool_bytes(const Shape& sh) { return size_t(sh.L) * sh.n_slots * sh.page_bytes; }
+size_t anchor_bytes(const Shape& sh) { return size_t(sh.L) * sh.anchor_page_bytes; }
 size_t table_bytes(const Shape& sh) {
   return (size_t(sh.n_frames) * sh.nt + size_t(sh.Hh) * sh.nh + size_t(sh.Ww) * sh.nw) *
          2 * sizeof(float);
@@ -184,7 +196,14 @@ void build_plan(const Shape& sh, uint64_t hash, int64_t k, wf_plan* p) {
   double per_layer = 6.0 * p->n_active * nhd;
   if (p->anchor.present) per_layer += 4.0 * nhd;
   if (p->anchor.capture) per_layer += 2.0 * nhd;
-  p->publish_bytes = double(sh.L) * per_layer * double(sh.elem);
+  per_layer *= double(sh.elem);
+  if (sh.dtype == WF_FP8) {
+    // pages hold one byte per element: per cell q,k,v,q_rot stay bf16 and
+    // K, Vt shrink to 1 byte; the anchor slot write shrinks likewise
+    per_layer -= 2.0 * p->n_active * nhd;
+    if (p->anchor.present) per_layer -= 2.0 * nhd;
+  }
+  p->publish_bytes = double(sh.L) * per_layer;
 }
 
 }  // namespace wf

@@ -9,7 +9,8 @@ import torch
 
 from . import wf
 
-TORCH_DTYPE = {wf.WF_F32: torch.float32, wf.WF_BF16: torch.bfloat16}
+# q/k/v/q_rot/out and anchor_raw element type; FP8 configs keep them bf16
+TORCH_DTYPE = {wf.WF_F32: torch.float32, wf.WF_BF16: torch.bfloat16, wf.WF_FP8: torch.bfloat16}
 
 
 class Session:
@@ -27,6 +28,9 @@ class Session:
         S, N, H, D, L = cfg.S, cfg.F * cfg.Hh * cfg.Ww, cfg.n_heads, cfg.head_dim, cfg.n_layers
         self.S, self.N, self.H, self.D, self.L = S, N, H, D, L
         self.n_slots = 4 + max(cfg.W, cfg.W + S if cfg.W_store < 0 else cfg.W_store) + 2 * S
+        self.page_bytes = self.pool_bytes // (L * self.n_slots)
+        self.T = (N + 63) // 64
+        self.Npad = 64 * self.T
         self.bufs = self.alloc_io() if io else None
 
     def alloc_io(self):
@@ -41,6 +45,15 @@ class Session:
         pool = self.pool.view(self.dtype).view(self.L, self.n_slots, 2 * hnd)
         p = pool[layer, slot]
         return p[:hnd].view(self.H, self.N, self.D), p[hnd:].view(self.H, self.D, self.N)
+
+    def fp8_page(self, layer: int, slot: int):
+        """(K8 [H][Npad][D], Vt8 [H][D][Npad], codes [H][T][2]) uint8 views of
+        one slot of an FP8 pool (codes: exponent + 127 of K, V per tile)."""
+        H, D, Np, T = self.H, self.D, self.Npad, self.T
+        p = self.pool.view(self.L, self.n_slots, self.page_bytes)[layer, slot]
+        kv = H * Np * D
+        return (p[:kv].view(H, Np, D), p[kv:2 * kv].view(H, D, Np),
+                p[2 * kv:2 * kv + 2 * H * T].view(H, T, 2))
 
     def anchor_page(self, layer: int):
         hnd = self.H * self.N * self.D

@@ -57,5 +57,8 @@ WAN13B_5STEP_ROLLING = WAN13B_5STEP.with_(name="wan1.3b_5step_rolling",
 WAN14B_4STEP = Workload("wan14b_4step", S=4, W=4, n_chunk=133, F=3, Hh=30, Ww=52,
                         n_heads=40, head_dim=128, n_layers=40, q_head_scale=True)
 
+# The same 1.3B round over FP8 (E4M3) pages (App. C.6 variant).
+WAN13B_4STEP_FP8 = WAN13B_4STEP.with_(name="wan1.3b_4step_fp8", dtype=wf.WF_FP8)
+
 ALL = {w.name: w for w in (TINY_FP32, WAN13B_4STEP, WAN13B_5STEP, WAN13B_5STEP_ROLLING,
-                           WAN14B_4STEP)}
+                           WAN14B_4STEP, WAN13B_4STEP_FP8)}

@@ -35,7 +35,7 @@
  *     one; App. B.8 "Index conventions").
  *   - Stage S is the store cell (k - S, S); stages 0..S-1 are denoising.
  *
- * Device layouts (element type = dtype: fp32 or bf16; D = head_dim,
+ * Device layouts (element type = dtype: fp32 or bf16, bf16 for FP8; D = head_dim,
  * H = n_heads, N = tokens per chunk = F * Hh * Ww, token n at frame
  * n / (Hh Ww), row (n / Ww) % Hh, column n % Ww):
  *   q, k, v, q_rot, out   per layer [S+1][N][H][D], indexed by stage; the
@@ -49,6 +49,22 @@
  *   pool                  [L][n_slots] pages, n_slots = 4 + max(W, W_store) + 2 S.
  *   anchor_raw            [L] pages holding chunk 0's unrotated K and its Vt.
  *   tables                fp32 cos/sin pairs written by wf_bind.
+ *
+ * FP8 pages (dtype WF_FP8; WF App. C.6 Eq. 20-21: K/V in 8 bits halve the
+ * payload).  q, k, v, q_rot, out and anchor_raw are bf16 as above; a pool
+ * page holds, with Npad = 64 T, T = ceil(N / 64):
+ *                         K8  [H][Npad][D]  E4M3 codes of RoPE(k) / 2^eK
+ *                         Vt8 [H][D][Npad]  E4M3 codes of v / 2^eV
+ *                         codes [H][T][2]   per 64-token tile: eK + 127, eV + 127
+ *                         rounded up to 256 bytes.  E4M3 is the OCP format
+ *                         (bias 7, max 448, no infinities), rounded to
+ *                         nearest even; e is the smallest integer with
+ *                         amax(tile) <= 448 * 2^e (0 for an all-zero tile).
+ *                         Tokens N..Npad-1 are zero and never attended.
+ *                         Attention quantises each bf16 q_rot row the same
+ *                         way (one exponent per row) and multiplies on the
+ *                         FP8 matrix cores; P is rounded to E4M3 for the PV
+ *                         product, the row sum uses P before rounding.
  */
 #ifndef WF_H
 #define WF_H
@@ -75,7 +91,11 @@ typedef enum {
   WF_EUNSUPPORTED = -6  /* valid config without a kernel instance           */
 } wf_status;
 
-typedef enum { WF_F32 = 0, WF_BF16 = 1 } wf_dtype;
+typedef enum {
+  WF_F32 = 0,   /* everything fp32                                           */
+  WF_BF16 = 1,  /* everything bf16 (fp32 accumulation)                       */
+  WF_FP8 = 2    /* bf16 tensors, FP8 E4M3 pages (see "FP8 pages" above)      */
+} wf_dtype;
 
 typedef enum {
   WF_MASK_WAVE = 0,    /* M_WF(s,j) = 1[j >= s]                 (WF §3.1 Eq. 4) */
@@ -176,9 +196,10 @@ wf_status wf_pool_bytes(const wf_config* cfg, size_t* pool_bytes,
  * on the host in fp64, stored as fp32) with a synchronous copy.  Sizes are
  * checked first (WF_ESMALL), then kernel support for the config
  * (WF_EUNSUPPORTED: bf16 needs head_dim 64 or 128, N % 8 == 0, N >= 64 and
- * one layer's slots below 4 GiB; fp32
- * needs head_dim % 4 == 0, head_dim <= 128 and N % 4 == 0).  Buffers must
- * be 16-byte aligned.  The handle keeps the pointers, not the memory. */
+ * one layer's slots below 4 GiB; FP8 needs head_dim 128, N % 8 == 0, one
+ * layer's slots below 4 GiB and (1 + max(W, W_store) + 1 + S) * T <= 4096;
+ * fp32 needs head_dim % 4 == 0, head_dim <= 128 and N % 4 == 0).  Buffers
+ * must be 16-byte aligned.  The handle keeps the pointers, not the memory. */
 wf_status wf_bind(wf_handle* h, void* d_pool, size_t pool_bytes,
                   void* d_anchor_raw, size_t anchor_bytes,
                   void* d_tables, size_t table_bytes);

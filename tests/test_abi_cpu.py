@@ -13,7 +13,7 @@ import re
 import pytest
 
 from chunk_causal_dit_round_amd import wf
-from chunk_causal_dit_round_amd.workloads import ALL, TINY_FP32, WAN13B_4STEP
+from chunk_causal_dit_round_amd.workloads import ALL, TINY_FP32, WAN13B_4STEP, WAN13B_4STEP_FP8
 from oracle import wf_plan as P
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -79,6 +79,42 @@ def test_pool_bytes():
     assert pool == 30 * 20 * page
     assert anc == 30 * page
     assert tab == (133 * 3 * 22 + 30 * 21 + 52 * 21) * 8
+
+
+def test_pool_bytes_fp8():
+    """FP8 pages: K8 [H][Npad][D] + Vt8 [H][D][Npad] + codes [H][T][2], rounded
+    up to 256 bytes; the anchor store keeps bf16 raw K and Vt."""
+    cfg = WAN13B_4STEP_FP8.config()
+    pool, anc, tab = wf.wf_pool_bytes(cfg)
+    T = (4680 + 63) // 64
+    page = -(-(2 * 12 * 64 * T * 128 + 2 * 12 * T) // 256) * 256
+    assert T == 74 and pool == 30 * 20 * page
+    assert anc == 30 * 2 * 4680 * 12 * 128 * 2
+    assert tab == wf.wf_pool_bytes(WAN13B_4STEP.config())[2]
+
+
+def test_plan_numbers_fp8():
+    h = wf.wf_create(WAN13B_4STEP_FP8.config())
+    p = wf.wf_round_plan(h, 13)
+    assert abs(p.flops - 1.7763e14) / 1.7763e14 < 1e-4
+    # per cell: q,k,v in (bf16) + q_rot out (bf16) + K, Vt out (1 byte);
+    # anchor: raw K, Vt in (bf16) + anchor slot out (1 byte)
+    nhd = 4680 * 12 * 128
+    assert p.publish_bytes == 30 * (5 * 10 + 6) * nhd
+    wf.wf_destroy(h)
+
+
+def test_fp8_unsupported_shapes():
+    fake = 1 << 20
+    for w in (WAN13B_4STEP_FP8.with_(head_dim=64), WAN13B_4STEP_FP8.with_(Ww=51),
+              # longest context 40 pages x 104 tiles > 4096 tiles
+              WAN13B_4STEP_FP8.with_(W=30, Hh=40, Ww=55)):
+        cfg = w.config()
+        h = wf.wf_create(cfg)
+        pb, ab, tb = wf.wf_pool_bytes(cfg)
+        assert wf.status_of(wf.wf_bind, h, fake, pb, fake, ab, fake, tb) == wf.WF_EUNSUPPORTED
+        assert wf.wf_last_error() != ""
+        wf.wf_destroy(h)
 
 
 BAD = [dict(S=0), dict(S=9), dict(W=-1), dict(W_store=-2), dict(anchor=2), dict(n_chunk=0),

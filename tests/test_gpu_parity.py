@@ -16,8 +16,9 @@ import pytest
 import torch
 
 from chunk_causal_dit_round_amd import wf
-from chunk_causal_dit_round_amd.workloads import (TINY_FP32, WAN13B_4STEP, WAN13B_5STEP,
-                                                  WAN13B_5STEP_ROLLING, WAN14B_4STEP, Workload)
+from chunk_causal_dit_round_amd.workloads import (TINY_FP32, WAN13B_4STEP, WAN13B_4STEP_FP8,
+                                                  WAN13B_5STEP, WAN13B_5STEP_ROLLING,
+                                                  WAN14B_4STEP, Workload)
 from wfcheck import Rollout, check_attention, check_publish
 
 pytestmark = pytest.mark.gpu
@@ -88,6 +89,62 @@ SMALL_BF16 = [
 def test_small_bf16_every_round(w):
     _log(f"{w.name}: {w.n_chunk + w.S} rounds")
     full_rollout(w)
+
+
+SMALL_FP8 = [
+    # FP8 pages: 360 tokens -> 6 tiles per page, the last with 40 keys;
+    # several query tiles with a ragged tail
+    Workload("fp8_s4_n360", S=4, W=4, n_chunk=12, F=3, Hh=10, Ww=12, n_heads=3,
+             head_dim=128, n_layers=2, dtype=wf.WF_FP8),
+    # N a multiple of 64: no padding tokens
+    Workload("fp8_s2_n128", S=2, W=2, n_chunk=8, F=2, Hh=8, Ww=8, n_heads=2,
+             head_dim=128, n_layers=1, dtype=wf.WF_FP8),
+    # 72 tokens: two tiles per page, the second with 8 keys
+    Workload("fp8_s2_n72", S=2, W=2, n_chunk=8, F=3, Hh=4, Ww=6, n_heads=2,
+             head_dim=128, n_layers=1, dtype=wf.WF_FP8),
+    # a single 64-token tile per page; Rolling-Forcing comparison mask
+    Workload("fp8_rolling_n64", S=3, W=2, n_chunk=7, F=1, Hh=8, Ww=8, n_heads=2,
+             head_dim=128, n_layers=1, mask=wf.WF_MASK_ROLLING, dtype=wf.WF_FP8),
+    # per-head query scale U(0.5, 2), no anchor
+    Workload("fp8_headscale", S=2, W=3, anchor=0, n_chunk=7, F=1, Hh=16, Ww=16, n_heads=4,
+             head_dim=128, n_layers=1, q_head_scale=True, dtype=wf.WF_FP8),
+]
+
+
+@pytest.mark.parametrize("w", SMALL_FP8, ids=lambda w: w.name)
+def test_small_fp8_every_round(w):
+    _log(f"{w.name}: {w.n_chunk + w.S} rounds")
+    ro = Rollout(w)
+    worst = 0.0
+    try:
+        for k in range(w.n_chunk + w.S):
+            ro.run(k)
+            for layer in range(w.n_layers):
+                check_publish(ro, k, layer)
+                worst = max(worst, check_attention(ro, k, layer))
+    finally:
+        ro.close()
+    _log(f"  max abs err {worst:.3e}")
+
+
+@pytest.mark.timeout(600)
+def test_full_size_wan13b_4step_fp8_sampled():
+    """The 1.3B 4-step round over FP8 pages: steady state with the anchor
+    re-rotated (k=14), first and last layer, 64 sampled rows per (group,
+    head) plus the last row; whole pages."""
+    w = WAN13B_4STEP_FP8
+    ro = Rollout(w)
+    try:
+        for k in range(15):
+            _log(f"{w.name} round {k}")
+            ro.run(k)
+            if k in (4, 14):
+                for layer in (0, w.n_layers - 1):
+                    check_publish(ro, k, layer)
+                    err = check_attention(ro, k, layer, rows=64)
+                    _log(f"  k={k} layer={layer} max abs err {err:.3e}")
+    finally:
+        ro.close()
 
 
 @pytest.mark.timeout(600)
