@@ -20,6 +20,9 @@ Other modes (one JSON line each):
                      full-width and whole-request rounds/s.
   --copy-calibration a plain device copy of known size, for scaling the HBM
                      FETCH_SIZE / WRITE_SIZE counters to bytes.
+  --workload wan1.3b_4step_fp8
+                     the same round over FP8 (E4M3) pages; roofline against the
+                     dense fp8 MFMA peak.
 """
 
 import argparse
@@ -34,6 +37,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBPS = 8000.0
 ATTN_SRC = os.path.join(ROOT, "chunk_causal_dit_round_amd", "csrc", "wf_attention.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_bf16_wan1.3b_4step_hbm_traffic.txt")
@@ -120,7 +124,7 @@ def rollout(w):
     print(json.dumps(res), flush=True)
 
 
-def oracle_baseline(w, k, layer, heads, raw):
+def oracle_baseline(w, k, layer, heads, raw, fp8=False):
     """Time the oracle on `heads` of one layer of round k (every group)."""
     import numpy as np  # noqa: F401
     from oracle import wf_plan as P
@@ -138,7 +142,7 @@ def oracle_baseline(w, k, layer, heads, raw):
     t0 = time.perf_counter()
     for s in range(w.S + 1):
         if P.chunk_active(oc, k - s):
-            WR.group_output(oc, k, s, layer, raw, heads=heads)
+            WR.group_output(oc, k, s, layer, raw, heads=heads, fp8=fp8)
     dt = time.perf_counter() - t0
     frac = len(heads) / (w.n_heads * w.n_layers)   # share of one round
     t_round = dt / frac
@@ -230,9 +234,13 @@ def main():
     pub_bytes_launch = plans[0].publish_bytes / L
     achieved = flops_launch / (att_avg * 1e-3) / 1e12
     total_flops = sum(p.flops for p in plans)
+    fp8 = w.dtype == wf.WF_FP8
+    peak = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
 
     res = {
-        "metric": "wavefront rounds/sec (=chunks/sec) and attention TFLOP/s vs bf16 MFMA peak",
+        "metric": ("wavefront rounds/sec (=chunks/sec) and attention TFLOP/s vs fp8 MFMA peak "
+                   "(FP8 E4M3 pages)" if fp8 else
+                   "wavefront rounds/sec (=chunks/sec) and attention TFLOP/s vs bf16 MFMA peak"),
         "value": args.steps / elapsed,
         "unit": "rounds/s",
         "n_gpus": 1,
@@ -242,17 +250,17 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8" if fp8 else "bf16",
         "data": "synthetic",
         "config": {"workload": f"{w.name} steady wavefront round", "S": w.S, "W": w.W,
                    "W_store": w_store, "anchor": w.anchor, "n_chunk": w.n_chunk,
                    "tokens_per_chunk": w.n_tokens, "heads": w.n_heads,
                    "head_dim": w.head_dim, "layers": L,
                    "rounds_timed": [k0, k0 + args.steps - 1], "n_rounds": n_rounds},
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": measured_traffic(),
-                     "kernel": "wf_attention_bf16_kernel<128>",
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak,
+                     "unit": "TFLOP/s", "frac": achieved / peak,
+                     "traffic": None if fp8 else measured_traffic(),
+                     "kernel": "wf_attention_fp8_kernel" if fp8 else "wf_attention_bf16_kernel<128>",
                      "flops_per_launch": flops_launch, "avg_launch_ms": att_avg},
         "attention_tflops_round": total_flops / elapsed / 1e12,
         "publish": {"avg_launch_ms": pub_avg, "bytes_per_launch": pub_bytes_launch,
@@ -265,7 +273,7 @@ def main():
             x = synth.slice_input("bench", rnd % 2, layer, stage, name, sess.N, sess.H, sess.D,
                                   dev, sess.dtype)
             return x.to(torch.float64).cpu().numpy()
-        res["cpu_baseline"] = oracle_baseline(w, k0, 0, list(range(args.cpu_heads)), raw)
+        res["cpu_baseline"] = oracle_baseline(w, k0, 0, list(range(args.cpu_heads)), raw, fp8=fp8)
     print(json.dumps(res), flush=True)
 
 

@@ -20,13 +20,18 @@
 //     32 h + 16 t2 + v of the tile: the lane's 32 values are then exactly
 //     the B operand bytes of the PV product (P^T, k = key), no lane exchange;
 //   * O^T = Vt P^T, A = Vt rows (value dims), keys contiguous.
-// Schedule: 8 waves in two groups of 4 alternate an MFMA cluster (PV of
-// tile t-1, QK of tile t) with a VALU cluster (softmax of tile t, staging of
-// the next tile), as in the bf16 instance.  K and Vt tiles live in a
+// Schedule: the 8 waves (32 query rows each) run in lockstep, one
+// work-group barrier per 64-key tile: an MFMA cluster (PV of tile t-1, row
+// sums, QK of tile t; 9 FP8 MFMAs) then the softmax of tile t and the
+// staging of tile t+2.  With the MFMA cluster this short, letting the two
+// waves of a SIMD drift between clusters measured faster than the bf16
+// instance's ping-pong between wave groups.  K and Vt tiles live in a
 // 4-stage LDS ring with 16-byte chunks XOR-swizzled per row (conflict-free
 // operand reads and stores).  Softmax in base 2 with lazy rescale; the
-// weights, biased by 2^7, are rounded to E4M3 (at most 2^8 < 448) for the
-// PV product and summed in fp32 before rounding.
+// weights, biased by 2^7, are rounded to E4M3 (at most 2^8 < 448).  The row
+// sum is one more FP8 MFMA of an all-ones operand against the same rounded
+// weights, so numerator and denominator use identical weights (and the
+// VALU, the bottleneck here, does no per-weight addition).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -112,7 +117,6 @@ __global__ __launch_bounds__(kNT, 1) void wf_attention_fp8_kernel(const AttnArgs
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int col = lane & 31, half = lane >> 5;
-  const int pgroup = wave >> 2;
   const int n_pages = G.n_pages;
   const int n_tiles = n_pages * T;
   const int last_valid = N - kBN * (T - 1);       // keys in the last tile of a page
@@ -206,10 +210,13 @@ __global__ __launch_bounds__(kNT, 1) void wf_attention_fp8_kernel(const AttnArgs
 #pragma unroll
   for (int i = 0; i < 4; ++i) oacc[i] = f32x16{};
   f32x16 sacc[2];
+  f32x16 lacc = f32x16{};                         // row sums: ones x P^T
   i32x8 pf = {};
+  i32x8 ones;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) ones[w] = 0x38383838;   // E4M3 1.0
   float m_run = -__builtin_inff();
   float mb = -__builtin_inff();                   // kBias - m_run
-  float l_run = 0.f;
   const float c = a.scale_log2e;
   int kcode = kE8M0One, vcode = kE8M0One;         // scales of the tiles in use
 
@@ -250,6 +257,9 @@ __global__ __launch_bounds__(kNT, 1) void wf_attention_fp8_kernel(const AttnArgs
       if (i < 4) {
         oacc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f, pf, oacc[i], 0, 0, 0, vcode, 0,
                                                                   kE8M0One);
+        if (i == 3)
+          lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pf, lacc, 0, 0, 0, kE8M0One, 0,
+                                                                 kE8M0One);
       } else {
         const int j = i - 4, s = j >> 1, t2 = j & 1;
         sacc[t2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f, qf[s], s == 0 ? f32x16{} : sacc[t2],
@@ -260,6 +270,7 @@ __global__ __launch_bounds__(kNT, 1) void wf_attention_fp8_kernel(const AttnArgs
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i == 3) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if (i + kAhead < NI) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
   };
@@ -283,21 +294,15 @@ __global__ __launch_bounds__(kNT, 1) void wf_attention_fp8_kernel(const AttnArgs
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       mb = kBias - m_new;
-      l_run *= alpha;
+      lacc *= alpha;
 #pragma unroll
       for (int i = 0; i < 4; ++i) oacc[i] *= alpha;
     }
     float p[2][16];
-    float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        p[t2][v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t2][v], c, mb));
-        if (v & 1) ls1 += p[t2][v];
-        else ls0 += p[t2][v];
-      }
-    l_run += ls0 + ls1;
+      for (int v = 0; v < 16; ++v) p[t2][v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t2][v], c, mb));
     // byte j = 16 t2 + v of the PV B operand
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
@@ -322,12 +327,14 @@ __global__ __launch_bounds__(kNT, 1) void wf_attention_fp8_kernel(const AttnArgs
   __syncthreads();
   kcode = tcode[0] & 0xff;
 
-  if (pgroup == 1) __syncthreads();
+  // One barrier per tile orders the LDS ring: a tile stored in the softmax
+  // phase of iteration t is first read two barriers later (cluster t+2), and
+  // the stage it overwrites was last read in cluster t-1, which every wave
+  // finished (LDS reads drained) before the barrier closing iteration t-1.
   bool staged = false;
   int ptp = 0;                                    // tile-in-page of the softmax's tile
   for (int t = 0; t <= n_tiles; ++t) {
     mfma_cluster((t - 1) & (kStages - 1), t & (kStages - 1));
-    __syncthreads();
     if (t < n_tiles) {
       if (staged) store_tile((t + 2) & (kStages - 1));
       staged = false;
@@ -342,12 +349,11 @@ __global__ __launch_bounds__(kNT, 1) void wf_attention_fp8_kernel(const AttnArgs
       kcode = tcode[nxt] & 0xff;
       vcode = tcode[t] >> 8;
     }
-    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0); __syncthreads(); __builtin_amdgcn_sched_barrier(0);
   }
-  if (pgroup == 0) __syncthreads();
 
   // ---- epilogue: O = (O^T)^T / l ----
-  const float inv = 1.f / pair_sum32(l_run);
+  const float inv = 1.f / lacc[0];
   if (q < N) {
     __bf16* orow = static_cast<__bf16*>(a.out) + ((static_cast<int64_t>(G.stage) * N + q) * H + h) * kD;
 #pragma unroll

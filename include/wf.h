@@ -63,8 +63,9 @@
  *                         Tokens N..Npad-1 are zero and never attended.
  *                         Attention quantises each bf16 q_rot row the same
  *                         way (one exponent per row) and multiplies on the
- *                         FP8 matrix cores; P is rounded to E4M3 for the PV
- *                         product, the row sum uses P before rounding.
+ *                         FP8 matrix cores; the softmax weights are
+ *                         rounded to E4M3 for the PV product and the row
+ *                         sum adds the same rounded weights.
  */
 #ifndef WF_H
 #define WF_H

@@ -124,7 +124,7 @@ def test_small_fp8_every_round(w):
                 worst = max(worst, check_attention(ro, k, layer))
     finally:
         ro.close()
-    _log(f"  max abs err {worst:.3e}")
+    _log(f"  max abs err {worst:.3e}, {ro.fp8_bound_ratio:.2f} x the FP8 bound at worst")
 
 
 @pytest.mark.timeout(600)
@@ -142,7 +142,8 @@ def test_full_size_wan13b_4step_fp8_sampled():
                 for layer in (0, w.n_layers - 1):
                     check_publish(ro, k, layer)
                     err = check_attention(ro, k, layer, rows=64)
-                    _log(f"  k={k} layer={layer} max abs err {err:.3e}")
+                    _log(f"  k={k} layer={layer} max abs err {err:.3e}, "
+                         f"{ro.fp8_bound_ratio:.2f} x the FP8 bound at worst")
     finally:
         ro.close()
 

@@ -29,18 +29,24 @@ def fp8_attention_tolerance(q8, k8, v8, scale):
     """Per-element bound on |O_gpu - O_oracle| over FP8 pages ([Nq, d] each).
 
     The oracle attends exactly over the dequantised Q, K and V.  The kernel
-    in addition rounds every softmax weight P_k to E4M3 for the PV product
-    (relative error |eps_k| <= 2^-4; the row sum uses the unrounded weight),
-    so O_gpu - O = sum_k eps_k P_k V_k / sum_k P_k.  With the eps_k treated
-    as independent and uniform (standard deviation 2^-4 / sqrt 3), six
-    standard deviations of that sum, plus 1e-3 for fp32 accumulation and the
-    rare one-code differences between the kernel's fp32 and the oracle's
-    fp64 rotation of Q and K.
+    in addition rounds every softmax weight P_k to E4M3 (relative error
+    |eps_k| <= 2^-4) and uses the rounded weights in both the PV product and
+    the row sum, so O_gpu - O = sum_k eps_k P_k (V_k - O) / sum_k P_k (1 +
+    eps_k).  With the eps_k treated as independent and uniform (standard
+    deviation 2^-4 / sqrt 3), six standard deviations of that sum (its
+    denominator bounded below by (1 - 2^-4) sum_k P_k), plus 1e-3 for fp32
+    accumulation and the rare one-code differences between the kernel's fp32
+    and the oracle's fp64 rotation of Q and K.
     """
     s = scale * (q8 @ k8.T)
     s -= s.max(axis=1, keepdims=True)
     p = np.exp(s)
-    spread = np.sqrt((p * p) @ (v8 * v8)) / p.sum(axis=1, keepdims=True)
+    ps = p.sum(axis=1, keepdims=True)
+    o = (p @ v8) / ps
+    # sum_k P_k^2 (V_kd - O_d)^2 = P^2 V^2 - 2 O (P^2 V) + O^2 sum P^2
+    p2 = p * p
+    var = p2 @ (v8 * v8) - 2.0 * o * (p2 @ v8) + o * o * p2.sum(axis=1, keepdims=True)
+    spread = np.sqrt(np.maximum(var, 0.0)) / (ps * (1.0 - 2.0 ** -4))
     return 6.0 * 2.0 ** -4 / math.sqrt(3.0) * spread + 1e-3
 
 
@@ -251,6 +257,7 @@ def check_attention(ro, k, layer, rows=None, heads=None, stages=None, seed=0):
                                                         WR.scale_of(oc))
             ratio = (err / tol).max()
             worst = max(worst, err.max())
+            ro.fp8_bound_ratio = max(getattr(ro, "fp8_bound_ratio", 0.0), ratio)
             assert ratio <= 1.0, (f"attention k={k} l={layer} s={st}: max abs err "
                                   f"{err.max():.3e}, {ratio:.2f} x the FP8 bound")
             continue
