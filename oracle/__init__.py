@@ -17,9 +17,11 @@ wf_rope       3D rotary position embedding in fp64
 wf_attention  dense softmax attention in fp64
 wf_fp8        FP8 (E4M3) page and query quantisation reading
 wf_round      one round assembled by logical chunk identity (never by slot)
+wf_dit        Wan-shaped DiT block around the round (norms, projections, FFN)
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against printed values, closed forms, invariants or library routines
 (torch CPU ``scaled_dot_product_attention``, complex multiplication,
-torch's ``float8_e4m3fn``).
+torch's ``float8_e4m3fn``, torch's fp64 norms and GELU, a block composed of
+torch modules).
 """
