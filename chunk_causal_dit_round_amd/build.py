@@ -17,7 +17,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libwf.so")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["wf_runtime.cpp", "wf_publish.hip", "wf_attention.hip", "wf_attention_fp8.hip"]
+HIP_SOURCES = ["wf_runtime.cpp", "wf_publish.hip", "wf_attention.hip", "wf_attention_fp8.hip",
+               "wf_dit.hip", "wf_dit.cpp"]
 # Attention scores are finite or -inf, never NaN: without NaN semantics the
 # row max needs no canonicalising v_max x,x per score.
 FILE_FLAGS = {"wf_attention.hip": ["-fno-honor-nans"],
@@ -64,6 +65,9 @@ def build_library(verbose: bool = False) -> str:
               "-c", os.path.join(CSRC, src), "-o", obj], verbose)
         objs.append(obj)
     tmp = LIB + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    # the DiT block's products go through hipBLASLt (the process's copy of
+    # libhipblaslt.so.1: PyTorch's own when loaded from Python)
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp,
+          "-L/opt/rocm/lib", "-lhipblaslt"], verbose)
     os.replace(tmp, LIB)
     return LIB

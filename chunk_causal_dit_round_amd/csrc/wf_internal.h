@@ -1,0 +1,50 @@
+// Host-side internals shared by the C ABI entry points (wf_runtime.cpp for
+// the round, wf_dit.cpp for the DiT block around it).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "wf.h"
+#include "wf_plan.h"
+
+namespace wf {
+struct DitState;  // hipBLASLt handle and product plans, created on first use
+}
+
+struct wf_handle {
+  wf_config cfg;
+  wf::Shape sh;
+  uint64_t hash = 0;
+  int64_t next_k = 0;
+  void* pool = nullptr;
+  void* anchor = nullptr;
+  void* tables = nullptr;
+  bool bound = false;
+  std::vector<uint8_t> published;  // per layer, current round
+  wf::DitState* dit = nullptr;
+};
+
+namespace wf {
+
+// Frees the DiT state of a handle (no-op if none was created).
+void dit_release(wf_handle* h);
+
+namespace rt {
+
+wf_status fail(wf_status s, const std::string& why);
+wf_status ok();
+bool aligned16(const void* p);
+// The caller's plan checked against the handle; `fresh` receives the rebuilt plan.
+wf_status check_plan(const wf_handle* h, const wf_plan* p, wf_plan* fresh);
+wf_status check_layer_call(const wf_handle* h, int32_t layer);
+wf_status do_publish(wf_handle* h, const wf_plan& p, int layer, const void* q, const void* k,
+                     const void* v, void* q_rot, hipStream_t stream);
+wf_status do_attention(wf_handle* h, const wf_plan& p, int layer, const void* q_rot, void* out,
+                       hipStream_t stream);
+
+}  // namespace rt
+}  // namespace wf

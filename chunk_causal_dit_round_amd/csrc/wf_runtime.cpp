@@ -12,24 +12,18 @@
 #include <vector>
 
 #include "wf.h"
+#include "wf_internal.h"
 #include "wf_kernels.h"
 #include "wf_plan.h"
-
-struct wf_handle {
-  wf_config cfg;
-  wf::Shape sh;
-  uint64_t hash = 0;
-  int64_t next_k = 0;
-  void* pool = nullptr;
-  void* anchor = nullptr;
-  void* tables = nullptr;
-  bool bound = false;
-  std::vector<uint8_t> published;  // per layer, current round
-};
 
 namespace {
 
 thread_local std::string g_last_error;
+
+}  // namespace
+
+namespace wf {
+namespace rt {
 
 wf_status fail(wf_status s, const std::string& why) {
   g_last_error = why;
@@ -182,7 +176,10 @@ wf_status check_layer_call(const wf_handle* h, int32_t layer) {
   return ok();
 }
 
-}  // namespace
+}  // namespace rt
+}  // namespace wf
+
+using namespace wf::rt;
 
 extern "C" {
 
@@ -217,7 +214,10 @@ wf_status wf_create(const wf_config* cfg, wf_handle** out) {
   return ok();
 }
 
-void wf_destroy(wf_handle* h) { delete h; }
+void wf_destroy(wf_handle* h) {
+  if (h) wf::dit_release(h);
+  delete h;
+}
 
 wf_status wf_pool_bytes(const wf_config* cfg, size_t* pool, size_t* anchor, size_t* tables) {
   wf::Shape sh;

@@ -9,6 +9,7 @@ Values: N(0, 1) drawn in fp32 by torch's generator on the target device,
 optionally scaled per head (q only), then cast to the round dtype.
 """
 
+import math
 import zlib
 
 import torch
@@ -65,3 +66,41 @@ def fill_round(bufs: dict, tag: str, rnd: int, n_layers: int, n_stages: int,
             for name in NAMES:
                 bufs[name][layer, s].copy_(slice_input(tag, rnd, layer, s, name, n, hh, d,
                                                        q.device, q.dtype, q_scale))
+
+
+# ---- DiT block around the round: dummy (random-init) weights and inputs ----
+def _gen(device, *parts):
+    g = torch.Generator(device=device)
+    g.manual_seed(seed_of(BASE_SEED, *parts))
+    return g
+
+
+def dit_layer_weights(tag: str, layer: int, C: int, F: int, device) -> dict:
+    """One layer's weights: W [out][in] ~ N(0, 1/in) in bf16; biases
+    ~ N(0, 0.1^2), RMSNorm gains ~ 1 + N(0, 0.1^2), fp32."""
+    g = _gen(device, tag, "dit-weights", layer)
+
+    def mat(o, i):
+        return (torch.randn((o, i), generator=g, device=device) / math.sqrt(i)).to(torch.bfloat16)
+
+    def vec(n, base=0.0):
+        return base + 0.1 * torch.randn(n, generator=g, device=device)
+
+    return dict(w_qkv=mat(3 * C, C), b_qkv=vec(3 * C), g_q=vec(C, 1.0), g_k=vec(C, 1.0),
+                w_o=mat(C, C), b_o=vec(C), w_1=mat(F, C), b_1=vec(F), w_2=mat(C, F), b_2=vec(C))
+
+
+def dit_modulation(tag: str, layer: int, n_stages: int, C: int, device) -> torch.Tensor:
+    """[S+1][6][C] fp32 (shift1, scale1, gate1, shift2, scale2, gate2) per
+    stage: N(0, 0.1^2), gates centred on 0.5."""
+    g = _gen(device, tag, "dit-mod", layer)
+    m = 0.1 * torch.randn((n_stages, 6, C), generator=g, device=device)
+    m[:, 2] += 0.5
+    m[:, 5] += 0.5
+    return m
+
+
+def dit_x0(tag: str, rnd: int, stage: int, n_tokens: int, C: int, device) -> torch.Tensor:
+    """Layer-0 input [N][C] of the cell at ``stage`` in round ``rnd``: N(0, 1), fp32."""
+    g = _gen(device, tag, "dit-x0", rnd, stage)
+    return torch.randn((n_tokens, C), generator=g, device=device)

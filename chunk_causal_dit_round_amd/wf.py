@@ -50,6 +50,15 @@ class wf_plan(ctypes.Structure):
                 ("kv_tokens", i64), ("flops", f64), ("publish_bytes", f64)]
 
 
+class wf_dit_config(ctypes.Structure):
+    _fields_ = [("ffn_dim", i32), ("reserved", i32), ("eps", f64)]
+
+
+class wf_dit_weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("w_qkv", "b_qkv", "g_q", "g_k", "w_o", "b_o", "w_1", "b_1", "w_2", "b_2")]
+
+
 class WfError(RuntimeError):
     def __init__(self, status, detail):
         super().__init__(f"{_strerror(status)} ({status}): {detail}")
@@ -82,6 +91,11 @@ def _load():
         "wf_wave_attention": (i32, [H, ctypes.POINTER(wf_plan), i32, cvp, vp, vp]),
         "wf_round_commit": (i32, [H, ctypes.POINTER(wf_plan)]),
         "wf_round": (i32, [H, ctypes.POINTER(wf_plan), cvp, cvp, cvp, vp, vp, vp]),
+        "wf_dit_workspace_bytes": (i32, [H, ctypes.POINTER(wf_dit_config), ctypes.POINTER(sz)]),
+        "wf_dit_layer": (i32, [H, ctypes.POINTER(wf_plan), i32, ctypes.POINTER(wf_dit_config),
+                               ctypes.POINTER(wf_dit_weights), cvp, vp, vp, sz, vp]),
+        "wf_dit_round": (i32, [H, ctypes.POINTER(wf_plan), ctypes.POINTER(wf_dit_config),
+                               ctypes.POINTER(wf_dit_weights), cvp, vp, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -190,6 +204,38 @@ def wf_round_commit(h, plan):
 def wf_round(h, plan, q, k, v, q_rot, out, stream=None):
     _check(_lib.wf_round(h, ctypes.byref(plan), _ptr(q), _ptr(k), _ptr(v), _ptr(q_rot),
                          _ptr(out), _stream(stream)))
+
+
+def make_dit_config(ffn_dim, eps=0.0):
+    return wf_dit_config(ffn_dim=ffn_dim, reserved=0, eps=eps)
+
+
+def make_dit_weights(layers):
+    """Array of wf_dit_weights from dicts of tensors (one dict per layer)."""
+    arr = (wf_dit_weights * len(layers))()
+    for i, d in enumerate(layers):
+        for n, _ in wf_dit_weights._fields_:
+            setattr(arr[i], n, _ptr(d[n]))
+    return arr
+
+
+def wf_dit_workspace_bytes(h, dc):
+    b = ctypes.c_size_t()
+    _check(_lib.wf_dit_workspace_bytes(h, ctypes.byref(dc), ctypes.byref(b)))
+    return b.value
+
+
+def wf_dit_layer(h, plan, layer, dc, weights, mod, x, work, work_bytes, stream=None):
+    """``weights``: a wf_dit_weights (or an array whose element ``layer`` is used)."""
+    w = weights[layer] if isinstance(weights, ctypes.Array) else weights
+    _check(_lib.wf_dit_layer(h, ctypes.byref(plan), layer, ctypes.byref(dc), ctypes.byref(w),
+                             _ptr(mod), _ptr(x), _ptr(work), work_bytes, _stream(stream)))
+
+
+def wf_dit_round(h, plan, dc, weights, mod, x, work, work_bytes, stream=None):
+    """``weights``: an array of wf_dit_weights, one per layer."""
+    _check(_lib.wf_dit_round(h, ctypes.byref(plan), ctypes.byref(dc), weights, _ptr(mod),
+                             _ptr(x), _ptr(work), work_bytes, _stream(stream)))
 
 
 def status_of(fn, *args, **kw):

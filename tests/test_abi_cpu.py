@@ -20,14 +20,19 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def header_functions():
-    text = open(os.path.join(ROOT, "include", "wf.h")).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(wf_[a-z_]+)\s*\(", text)))
+    names = set()
+    for f in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if f.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", f)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(wf_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 13, names
+    assert len(names) == 16, names
+    assert {"wf_dit_workspace_bytes", "wf_dit_layer", "wf_dit_round"} <= set(names)
     lib = ctypes.CDLL(wf.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -191,3 +196,39 @@ def test_strerror():
     for s in range(0, -7, -1):
         assert wf.wf_strerror(s) and wf.wf_strerror(s) != "unknown status"
     assert wf.wf_strerror(-99) == "unknown status"
+
+
+def test_dit_workspace_bytes_and_errors_before_device_work():
+    cfg = WAN13B_4STEP.config()
+    h = wf.wf_create(cfg)
+    fake = 1 << 20    # never dereferenced
+    try:
+        dc = wf.make_dit_config(8960)
+        got = wf.wf_dit_workspace_bytes(h, dc)
+        rows, C = 5 * 4680, 1536
+        up = lambda x: -(-x // 256) * 256  # noqa: E731
+        # a, qkv, q, k, v, q_rot, o (bf16), y (fp32), FFN hidden (bf16), GEMM workspace
+        want = (up(rows * C * 2) + up(rows * 3 * C * 2) + 5 * up(rows * C * 2) + up(rows * C * 4)
+                + up(rows * 8960 * 2) + (64 << 20))
+        assert got == want
+        for bad in (wf.make_dit_config(0), wf.make_dit_config(7), wf.make_dit_config(64, eps=-1.0)):
+            assert wf.status_of(wf.wf_dit_workspace_bytes, h, bad) == wf.WF_EINVAL
+        names = [n for n, _ in wf.wf_dit_weights._fields_]
+        W = wf.make_dit_weights([{n: fake for n in names} for _ in range(30)])
+        p0, p1 = wf.wf_round_plan(h, 0), wf.wf_round_plan(h, 1)
+        args = (fake, fake, fake, got)
+        assert wf.status_of(wf.wf_dit_layer, h, p1, 0, dc, W, *args, stream=0) == wf.WF_EORDER
+        assert wf.status_of(wf.wf_dit_round, h, p1, dc, W, *args, stream=0) == wf.WF_EORDER
+        assert wf.status_of(wf.wf_dit_layer, h, p0, 30, dc, W[0], *args, stream=0) == wf.WF_EINVAL
+        assert wf.status_of(wf.wf_dit_layer, h, p0, 0, dc, W, *args, stream=0) == wf.WF_EINVAL
+        assert "not bound" in wf.wf_last_error()
+        assert wf.status_of(wf.wf_dit_round, h, p0, dc, W, *args, stream=0) == wf.WF_EINVAL
+    finally:
+        wf.wf_destroy(h)
+    # C beyond the row kernels' limit
+    w = WAN13B_4STEP.with_(n_heads=72)
+    h = wf.wf_create(w.config())
+    try:
+        assert wf.status_of(wf.wf_dit_workspace_bytes, h, wf.make_dit_config(64)) == wf.WF_EUNSUPPORTED
+    finally:
+        wf.wf_destroy(h)

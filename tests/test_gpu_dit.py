@@ -1,0 +1,161 @@
+"""GPU parity of the DiT block around the round (``include/wf_dit.h``)
+against the fp64 oracle (``oracle/wf_dit.py``), through the C ABI.
+
+Small shapes: every round of a request, every active cell, every element of
+the residual stream after the last layer (two layers, so layer 1 reads
+layer 0's output and its own K/V pages).  Full 1.3B shape (one layer,
+FFN 8960): rounds 0..S+1 on the GPU, sampled token rows of every active cell
+of the last round checked against the oracle.
+
+Tolerance (derived from the arithmetic): each of the nine bf16 roundings on
+the way from x to the block's update d = x_out - x_in (a, qkv, q/k/v after
+the norms, q_rot and the K page, the softmax weights, o, a2, the FFN hidden
+activation) adds a relative error uniform in +-2^-9 that reaches the update
+with gain about one (norms are scale-free, the weights keep RMS, GELU' <=
+1.13, softmax weights lie in [0, 1]).  Treated as independent, they give
+sigma = 2^-9 / sqrt(3) * sqrt(9) * rms(d) per element of a row; the bar is
+6 sigma = 2.0e-2 * rms_row(d), plus 1e-5 for values of d near zero.
+"""
+
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+from chunk_causal_dit_round_amd import synth, wf
+from chunk_causal_dit_round_amd.dit import DitSession
+from chunk_causal_dit_round_amd.session import Session
+from chunk_causal_dit_round_amd.workloads import WAN13B_4STEP, Workload
+from oracle import wf_dit as D
+from wfcheck import oracle_cfg
+
+pytestmark = pytest.mark.gpu
+
+REL_TOL = 2.0e-2
+ABS_FLOOR = 1e-5
+
+
+@pytest.fixture(autouse=True)
+def _free_memory():
+    yield
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _oracle_rounds(ds: DitSession, w: Workload):
+    cfg = oracle_cfg(w)
+    weights = [D.Weights(**{n: t.detach().double().cpu().numpy() for n, t in lw.items()})
+               for lw in ds.layers]
+    mods = [m.double().cpu().numpy() for m in ds.mod]
+    x0 = lambda rnd, st: synth.dit_x0(ds.tag, rnd, st, w.n_tokens, ds.C, ds.s.device).double().cpu().numpy()  # noqa: E731
+    return D.DitRounds(cfg, x0, lambda l: weights[l], lambda l: mods[l])
+
+
+def _compare(got, want, x_in, what):
+    """Max error / bound over the rows; asserts the bound."""
+    d = want - x_in
+    rms = np.sqrt((d * d).mean(axis=1, keepdims=True))
+    bound = REL_TOL * rms + ABS_FLOOR
+    err = np.abs(got - want)
+    ratio = float((err / bound).max())
+    assert ratio <= 1.0, f"{what}: max err/bound {ratio:.3f}, max err {err.max():.3g}"
+    return ratio
+
+
+SMALL = [
+    # 72 tokens: one partial 256-row query tile, 64-key tiles straddle pages
+    (Workload("dit_s2_n72", S=2, W=2, n_chunk=6, F=3, Hh=4, Ww=6, n_heads=2, head_dim=64,
+              n_layers=2), 192),
+    # several query tiles + ragged tail, head_dim 128, anchor re-rotation
+    (Workload("dit_s4_n360", S=4, W=2, n_chunk=8, F=3, Hh=10, Ww=12, n_heads=2, head_dim=128,
+              n_layers=2), 512),
+]
+
+
+@pytest.mark.parametrize("w,ffn", SMALL, ids=[w.name for w, _ in SMALL])
+def test_small_dit_every_round(w, ffn):
+    s = Session(w.config(), io=False)
+    ds = DitSession(s, ffn, tag=w.name)
+    orc = _oracle_rounds(ds, w)
+    worst = 0.0
+    try:
+        for k in range(w.n_chunk + w.S):
+            plan = s.plan(k)
+            ds.load_x0(k)
+            ds.round(plan)
+            torch.cuda.synchronize()
+            got = ds.x.double().cpu().numpy()
+            for st in range(w.S + 1):
+                if not plan.cells[st].active:
+                    continue
+                want = orc.layer_output(k, w.n_layers - 1, st)
+                x_in = orc.x_in(k, 0, st)
+                worst = max(worst, _compare(got[st], want, x_in, f"{w.name} k={k} stage={st}"))
+        _log(f"{w.name}: worst err/bound {worst:.3f}")
+    finally:
+        s.close()
+
+
+def test_inactive_rows_untouched_and_layer_calls_equal_round():
+    """Rows of inactive stages keep their contents; wf_dit_layer per layer +
+    commit gives the same bits as wf_dit_round."""
+    w, ffn = SMALL[0]
+    outs = []
+    for mode in ("round", "layers"):
+        s = Session(w.config(), io=False)
+        ds = DitSession(s, ffn, tag=w.name)
+        try:
+            marker = torch.full_like(ds.x, 7.25)
+            for k in range(3):
+                plan = s.plan(k)
+                ds.x.copy_(marker)
+                ds.load_x0(k, [st for st in range(w.S + 1) if plan.cells[st].active])
+                if mode == "round":
+                    ds.round(plan)
+                else:
+                    for layer in range(w.n_layers):
+                        ds.layer(plan, layer)
+                    s.commit(plan)
+                torch.cuda.synchronize()
+                for st in range(w.S + 1):
+                    if not plan.cells[st].active:
+                        assert torch.equal(ds.x[st], marker[st])
+            outs.append(ds.x.clone())
+        finally:
+            s.close()
+    assert torch.equal(outs[0], outs[1])
+
+
+def test_full_size_wan13b_one_layer_sampled():
+    """1.3B shape (12 x 128 heads, C 1536, FFN 8960), one layer, rounds
+    0..S+1 (the last with the anchor present); 48 sampled rows per active
+    cell of the last round against the oracle."""
+    w = WAN13B_4STEP.with_(name="dit_wan1.3b_l1", n_layers=1)
+    s = Session(w.config(), io=False)
+    ds = DitSession(s, 8960, tag=w.name)
+    orc = _oracle_rounds(ds, w)
+    last = w.S + 1
+    try:
+        for k in range(last + 1):
+            plan = s.plan(k)
+            ds.load_x0(k)
+            ds.round(plan)
+        torch.cuda.synchronize()
+        got = ds.x.double().cpu().numpy()
+        rng = np.random.default_rng(13)
+        worst = 0.0
+        for st in range(w.S + 1):
+            rows = np.sort(rng.choice(w.n_tokens, 48, replace=False))
+            rows[-1] = w.n_tokens - 1
+            want = orc.layer_output(last, 0, st, rows=rows)
+            x_in = orc.x_in(last, 0, st)[rows]
+            worst = max(worst, _compare(got[st][rows], want, x_in, f"stage {st}"))
+        _log(f"{w.name}: worst err/bound {worst:.3f}")
+    finally:
+        s.close()
