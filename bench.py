@@ -23,6 +23,11 @@ Other modes (one JSON line each):
   --workload wan1.3b_4step_fp8
                      the same round over FP8 (E4M3) pages; roofline against the
                      dense fp8 MFMA peak.
+  --dit              the whole DiT forward of a steady round: every layer of the
+                     Wan-shaped block (norms, QKV / output / FFN products, qk norm,
+                     publish, attention) for all S+1 cells, dummy weights, FFN
+                     width --ffn (8960 for the 1.3B shape); whole-round TFLOP/s
+                     against the bf16 MFMA peak.
 """
 
 import argparse
@@ -67,6 +72,8 @@ def parse():
                     help="heads of one layer the oracle baseline times")
     ap.add_argument("--rollout", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--dit", action="store_true")
+    ap.add_argument("--ffn", type=int, default=0, help="DiT FFN width (0: 8960, or 13824 at 40 heads)")
     return ap.parse_args()
 
 
@@ -155,6 +162,122 @@ def oracle_baseline(w, k, layer, heads, raw, fp8=False):
                       f"{w.n_heads} heads); host has {cores} cores"}
 
 
+def dit_oracle_baseline(ds, w, k):
+    """Oracle time of one steady DiT round, assembled from timed pieces of
+    layer 0 (fp64): one cell's norm + QKV projection (full rows), the
+    attention of 256 sampled query rows of each stage over its full context,
+    and the output projection + FFN of those rows; scaled to N rows, S+1
+    cells and L layers."""
+    import numpy as np
+    import torch
+
+    from chunk_causal_dit_round_amd import synth
+    from oracle import wf_dit as D
+    from oracle import wf_plan as P
+    from oracle import wf_round as WR
+
+    oc = P.Config(S=w.S, W=w.W, W_store=w.W_store, anchor=w.anchor, n_chunk=w.n_chunk, F=w.F,
+                  Hh=w.Hh, Ww=w.Ww, n_heads=w.n_heads, head_dim=w.head_dim,
+                  n_layers=w.n_layers, mask=w.mask)
+    wt = D.Weights(**{n: t.double().cpu().numpy() for n, t in ds.layers[0].items()})
+    mod = ds.mod[0].double().cpu().numpy()
+    # round r starts from input set r % 2 on the GPU side
+    x0 = lambda rnd, st: synth.dit_x0(ds.tag, rnd % 2, st, w.n_tokens, ds.C, ds.s.device).double().cpu().numpy()  # noqa: E731
+    dr = D.DitRounds(oc, x0, lambda l: wt, lambda l: mod)
+    rows = np.arange(0, w.n_tokens, w.n_tokens // 256)[:256]
+    # projections of every page a steady round reads (one per cell and history page)
+    t0 = time.perf_counter()
+    dr.qkv(k, 0, 0)
+    t_proj = time.perf_counter() - t0
+    for st in range(w.S + 1):                      # the rest, untimed: shared inputs
+        for kind, chunk, _ in P.key_entries(oc, k, st):
+            rnd, cell, _f = WR.entry_source(oc, k, kind, chunk)
+            dr.qkv(rnd, 0, cell)
+    t_attn = t_fin = 0.0
+    for st in range(w.S + 1):
+        t0 = time.perf_counter()
+        o = dr.attention(k, 0, st, rows=rows)
+        t_attn += time.perf_counter() - t0
+        t0 = time.perf_counter()
+        D.finish_block(wt, dr.x_in(k, 0, st)[rows], mod[st], o)
+        t_fin += time.perf_counter() - t0
+    scale = w.n_tokens / len(rows)
+    t_layer = (w.S + 1) * t_proj + (t_attn + t_fin) * scale
+    t_round = t_layer * w.n_layers
+    cores = len(os.sched_getaffinity(0))
+    torch.cuda.synchronize()
+    return {"value": 1.0 / t_round, "unit": "rounds/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 oracle, layer 0 of round {k}: one cell's norm + QKV projection "
+                      f"{t_proj:.1f} s (x {w.S + 1} cells), attention + output projection + FFN "
+                      f"of {len(rows)} query rows per cell {t_attn + t_fin:.1f} s (x {scale:.1f}); "
+                      f"one layer {t_layer:.0f} s, x {w.n_layers} layers"}
+
+
+def dit_bench(args, w):
+    """Steady whole-DiT rounds: wf_dit_round over all layers."""
+    import torch
+
+    from chunk_causal_dit_round_amd import synth
+    from chunk_causal_dit_round_amd.dit import DitSession
+    from chunk_causal_dit_round_amd.session import Session
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ffn = args.ffn or (13824 if w.n_heads == 40 else 8960)
+    sess = Session(w.config(), device=dev, io=False)
+    ds = DitSession(sess, ffn, tag="bench-dit")
+    S, L, N, C = w.S, w.n_layers, w.n_tokens, ds.C
+    w_store = w.W + w.S if w.W_store < 0 else w.W_store
+    k_steady = w.S + max(w.W, w_store) + 1
+    if k_steady + args.warmup + args.steps > w.n_chunk:
+        print("steps + warmup exceed the steady rounds of one request", file=sys.stderr)
+        sys.exit(2)
+    # two resident layer-0 input sets; round r starts from set r % 2
+    x_sets = []
+    for i in range(2):
+        ds.load_x0(i)
+        x_sets.append(ds.x.clone())
+    stream = torch.cuda.current_stream()
+
+    def run(k):
+        ds.x.copy_(x_sets[k % 2])
+        plan = sess.plan(k)
+        ds.round(plan, stream)
+        return plan
+
+    for k in range(k_steady + args.warmup):
+        run(k)
+    torch.cuda.synchronize()
+    k0 = k_steady + args.warmup
+    t0 = time.perf_counter()
+    plans = [run(k0 + i) for i in range(args.steps)]
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    M = (S + 1) * N
+    gemm_flops = 2.0 * M * C * (3 * C + C + 2 * ffn) * L
+    attn_flops = plans[0].flops
+    total = (gemm_flops + attn_flops) * args.steps
+    achieved = total / elapsed / 1e12
+    res = {
+        "mode": "dit",
+        "metric": "DiT rounds/sec (=chunks/sec): whole Wan-shaped DiT forward of a wavefront round",
+        "value": args.steps / elapsed, "unit": "rounds/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": 1e3 * elapsed / args.steps, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{w.name} steady round, whole DiT forward (dummy weights)",
+                   "S": S, "W": w.W, "W_store": w_store, "tokens_per_chunk": N, "heads": w.n_heads,
+                   "head_dim": w.head_dim, "dim": C, "ffn_dim": ffn, "layers": L,
+                   "rounds_timed": [k0, k0 + args.steps - 1]},
+        "flops_per_round": {"products": gemm_flops, "attention": attn_flops},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "kernel": "whole round (products + attention)"},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = dit_oracle_baseline(ds, w, k0)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -173,6 +296,9 @@ def main():
         return
     if args.rollout:
         rollout(w)
+        return
+    if args.dit:
+        dit_bench(args, w)
         return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
