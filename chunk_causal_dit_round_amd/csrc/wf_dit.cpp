@@ -184,8 +184,7 @@ wf_status check_call(wf_handle* h, const wf_dit_config* dc, const wf_dit_weights
   wf_status s = check_dc(h, dc);
   if (s != WF_OK) return s;
   if (!h->bound) return fail(WF_EINVAL, "handle is not bound (call wf_bind first)");
-  if (h->sh.dtype != WF_BF16 && h->sh.dtype != WF_FP8)
-    return fail(WF_EUNSUPPORTED, "the DiT block runs bf16 and FP8 rounds only");
+  if (h->sh.dtype != WF_BF16) return fail(WF_EUNSUPPORTED, "the DiT block runs bf16 rounds only");
   if (!w || !mod || !x || !work) return fail(WF_EINVAL, "weights, mod, x or work is NULL");
   if (!aligned16(mod) || !aligned16(x) || !aligned16(work))
     return fail(WF_EINVAL, "mod, x and work must be 16-byte aligned");

@@ -37,8 +37,9 @@
  * Ownership and errors follow wf.h.  One difference: the first call on a
  * handle creates a hipBLASLt handle (its own small host and device state,
  * freed by wf_destroy); the products run through hipBLASLt, every other step
- * through this library's kernels.  Only bf16 and FP8 rounds have this block
- * (WF_EUNSUPPORTED for fp32); C must be a multiple of 8 and at most 8192.
+ * through this library's kernels.  Only bf16 rounds have this block
+ * (WF_EUNSUPPORTED for fp32 and FP8 pages); C must be a multiple of 8 and at
+ * most 8192.
  */
 #ifndef WF_DIT_H
 #define WF_DIT_H
