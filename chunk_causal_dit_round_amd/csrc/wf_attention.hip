@@ -11,7 +11,8 @@
 // key counts; groups are ordered longest first.
 //
 // bf16 instance (D = 64 or 128), CDNA4 MFMA v_mfma_f32_32x32x16_bf16:
-//   * work item = (group, head, 128 query rows); 4 waves x 32 queries.
+//   * work item = (group, head, 256 query rows); 8 waves x 32 queries, in two
+//     groups of 4 (waves i and i+4 share a SIMD).
 //   * S^T = K Q^T: A = 32 keys x 16 dims of K from LDS, B = Q fragments held
 //     in registers for the whole item.  Each lane ends up owning one query
 //     (its column), so the row max is an in-lane reduction plus one
@@ -23,11 +24,16 @@
 //     the PV MFMA without any lane exchange.
 //   * O^T = Vt P^T: A = 32 value dims x 16 keys read from the Vt tile (keys
 //     contiguous in the page layout), fp32 accumulation in registers.
-//   * K and Vt tiles (64 keys) are double-buffered in LDS (64 KB per
-//     work-group, two work-groups per CU); the next tile's global loads are
-//     in flight while the current one is multiplied.  16-byte chunks are
-//     XOR-swizzled per row so the MFMA operand reads spread over banks.
-//   * Online softmax in base 2 with the scale folded into one FMA.
+//   * K and Vt tiles (64 keys) pass through a 4-stage LDS ring (140 KB, one
+//     work-group per CU).  Rows are padded by one 16-byte chunk, which makes
+//     the operand reads conflict-free.  Tile t+3 is fetched into registers
+//     while tile t is multiplied and written to LDS one tile later, so no
+//     load latency is waited on.
+//   * Ping-pong: both wave groups run the same sequence of MFMA and softmax
+//     clusters, one cluster apart, so on every SIMD one wave issues MFMAs
+//     while the other runs the softmax.
+//   * Online softmax in base 2 with the scale folded into one FMA per score;
+//     O and l are rescaled only when a row max grows by more than 2^8.
 //
 // fp32 instance (head_dim <= 128, % 4): a plain tiled kernel (4 lanes per
 // query, 32-key LDS tiles, fp32 FMA), used for fp32 rounds.
@@ -55,16 +61,6 @@ __device__ inline int find_group(const AttnArgs& a, int item) {
 
 // A-operand row order for the QK MFMA: swaps bits 2 and 3.
 __device__ inline int perm_row(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
-
-// Chunk swizzles of the LDS tiles (16-byte chunk index XOR f(row)).  The
-// MFMA operand reads of lanes 0..15 touch K rows pi(0..15) and Vt rows
-// 0..15 at one logical chunk; both swizzles make every aligned group of 8
-// lanes hit 8 distinct chunks modulo 8 and every group of 16 lanes hit 16
-// distinct 16-byte bank groups, so the reads are conflict-free for either
-// bank width.
-template <int KCH>
-__device__ inline int kswz(int r) { return perm_row(r & 15) & (KCH - 1); }
-__device__ inline int vswz(int d) { return (d & 7) ^ ((d >> 3) & 1); }
 
 // v_permlane32_swap exchanges the upper half of its first operand with the
 // lower half of its second.  With both operands = x the two results hold, in
