@@ -27,7 +27,8 @@ Other modes (one JSON line each):
                      Wan-shaped block (norms, QKV / output / FFN products, qk norm,
                      publish, attention) for all S+1 cells, dummy weights, FFN
                      width --ffn (8960 for the 1.3B shape); whole-round TFLOP/s
-                     against the bf16 MFMA peak.
+                     against the bf16 MFMA peak.  With --rollout: the whole
+                     133-chunk request through the DiT.
 """
 
 import argparse
@@ -213,6 +214,47 @@ def dit_oracle_baseline(ds, w, k):
                       f"one layer {t_layer:.0f} s, x {w.n_layers} layers"}
 
 
+def dit_rollout(args, w):
+    """Every round of one request through the whole DiT (fresh seeded layer-0
+    inputs per round, generated between rounds and untimed)."""
+    import torch
+
+    from chunk_causal_dit_round_amd.dit import DitSession
+    from chunk_causal_dit_round_amd.session import Session
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ffn = args.ffn or (13824 if w.n_heads == 40 else 8960)
+    sess = Session(w.config(), device=dev, io=False)
+    ds = DitSession(sess, ffn, tag="rollout-dit")
+    n_rounds = w.n_chunk + w.S
+    w_store = w.W + w.S if w.W_store < 0 else w.W_store
+    k_steady = w.S + max(w.W, w_store) + 1
+    stream = torch.cuda.current_stream()
+    times = []
+    for k in range(n_rounds):
+        ds.load_x0(k)
+        plan = sess.plan(k)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        ds.round(plan, stream)
+        e1.record(stream)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1) / 1e3)
+        if k % 20 == 0:
+            print(f"# DiT rollout round {k}: {times[-1] * 1e3:.1f} ms", file=sys.stderr, flush=True)
+    steady = times[k_steady:w.n_chunk]
+    res = {"mode": "dit_rollout", "metric": "DiT rounds/sec (=chunks/sec), whole request",
+           "workload": f"{w.name} long rollout through the whole DiT (dummy weights, FFN {ffn}), "
+                       f"{w.n_chunk} chunks, {n_rounds} rounds",
+           "steady_rounds_per_s": 1.0 / statistics.median(steady),
+           "request_chunks_per_s": w.n_chunk / sum(times),
+           "request_seconds": sum(times),
+           "latent_frames_per_s": w.n_chunk * w.F / sum(times),
+           "slowest_round_ms": max(times) * 1e3, "fastest_round_ms": min(times) * 1e3}
+    print(json.dumps(res), flush=True)
+
+
 def dit_bench(args, w):
     """Steady whole-DiT rounds: wf_dit_round over all layers."""
     import torch
@@ -294,11 +336,14 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
-    if args.rollout:
+    if args.rollout and not args.dit:
         rollout(w)
         return
     if args.dit:
-        dit_bench(args, w)
+        if args.rollout:
+            dit_rollout(args, w)
+        else:
+            dit_bench(args, w)
         return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
