@@ -31,7 +31,8 @@
 //     load latency is waited on.
 //   * Ping-pong: both wave groups run the same sequence of MFMA and softmax
 //     clusters, one cluster apart, so on every SIMD one wave issues MFMAs
-//     while the other runs the softmax.
+//     while the other runs the softmax; the MFMA wave runs at raised issue
+//     priority (s_setprio).
 //   * Online softmax in base 2 with the scale folded into one FMA per score;
 //     O and l are rescaled only when a row max grows by more than 2^8.
 //
@@ -337,7 +338,11 @@ __global__ __launch_bounds__(512, 1) void wf_attention_bf16_kernel(const AttnArg
   if (pgroup == 1) __syncthreads();
   bool staged = false;
   for (int t = 0; t <= n_tiles; ++t) {
+    // The wave in its MFMA cluster gets issue priority over the SIMD's other
+    // wave (in its softmax cluster), so the matrix core is fed first.
+    __builtin_amdgcn_s_setprio(1);
     mfma_cluster((t - 1) & (STAGES - 1), t & (STAGES - 1));
+    __builtin_amdgcn_s_setprio(0);
     __syncthreads();
     if (t < n_tiles) {
       // tile t+2 was fetched into registers one tile ago; its stage last
