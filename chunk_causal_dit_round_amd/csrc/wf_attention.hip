@@ -33,8 +33,10 @@
 //     clusters, one cluster apart, so on every SIMD one wave issues MFMAs
 //     while the other runs the softmax; the MFMA wave runs at raised issue
 //     priority (s_setprio).
-//   * Online softmax in base 2 with the scale folded into one FMA per score;
-//     O and l are rescaled only when a row max grows by more than 2^8.
+//   * Online softmax in base 2.  The Q fragments carry the scale and the QK
+//     accumulators start from minus the running max, so the product is
+//     already the exponent of P.  O and l are rescaled only when a row max
+//     grows by more than 2^8.
 //
 // fp32 instance (head_dim <= 128, % 4): a plain tiled kernel (4 lanes per
 // query, 32-key LDS tiles, fp32 FMA), used for fp32 rounds.
@@ -137,9 +139,16 @@ __global__ __launch_bounds__(512, 1) void wf_attention_bf16_kernel(const AttnArg
   const int qc = q < N ? q : N - 1;
   const __bf16* qrow = static_cast<const __bf16*>(a.q_rot) +
                        ((static_cast<int64_t>(G.stage) * N + qc) * H + h) * D;
+  // The fragments are pre-multiplied by c = scale * log2(e) (and rounded to
+  // bf16 again), so S^T comes out in base-2 exponent units.
+  const float c = a.scale_log2e;
   bf16x8 qf[KSTEPS];
 #pragma unroll
-  for (int s = 0; s < KSTEPS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * half);
+  for (int s = 0; s < KSTEPS; ++s) {
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * half);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qf[s][e] = static_cast<__bf16>(static_cast<float>(x[e]) * c);
+  }
 
   // Per-thread load assignment: K rows kr0 + i*KROWS, chunk kc; Vt rows
   // (value dims) vd0 + i*VROWS, keys 8*vc .. 8*vc+7 of the tile.
@@ -220,9 +229,11 @@ __global__ __launch_bounds__(512, 1) void wf_attention_bf16_kernel(const AttnArg
   for (int i = 0; i < DT; ++i) oacc[i] = f32x16{};
   f32x16 sacc[2];
   bf16x8 pf[2][2];
-  float m_run = -__builtin_inff();
+  // The QK accumulators start from moff = -m (m = this lane's running max),
+  // so they hold c s - m and P = exp2(S) needs no per-score arithmetic.
+  f32x16 moff = f32x16{};
+  bool first_tile = true;
   float l_run = 0.f;
-  const float c = a.scale_log2e;
   const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
 
   // ---- MFMA cluster: O^T += Vt(t-1) P(t-1)^T, then S^T(t) = K(t) Q^T.
@@ -254,7 +265,7 @@ __global__ __launch_bounds__(512, 1) void wf_attention_bf16_kernel(const AttnArg
         oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, pf[kk >> 1][kk & 1], oacc[dt], 0, 0, 0);
       } else {
         const int j = i - NPV, s = j >> 1, t2 = j & 1;
-        sacc[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qf[s], s == 0 ? f32x16{} : sacc[t2], 0, 0, 0);
+        sacc[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qf[s], s == 0 ? moff : sacc[t2], 0, 0, 0);
       }
     }
     // order: kAhead LDS reads, then (MFMA, LDS read) pairs, then MFMAs
@@ -276,23 +287,40 @@ __global__ __launch_bounds__(512, 1) void wf_attention_bf16_kernel(const AttnArg
         for (int v = 0; v < 16; ++v)
           if (32 * t2 + 16 * (v >> 3) + 8 * half + (v & 7) >= valid) sacc[t2][v] = -__builtin_inff();
     }
-    float mx = fmaxf(sacc[0][0], sacc[1][0]);
+    // max of the lane's 32 values (c s - m) as a tree of 3-input maxima
+    float r[11];
 #pragma unroll
-    for (int v = 1; v < 16; ++v) mx = fmaxf(mx, fmaxf(sacc[0][v], sacc[1][v]));
-    mx = pair_max32(mx) * c;
-    if (__any(mx > m_run + kRescale)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
+    for (int i = 0; i < 10; ++i) {
+      const int a0 = 3 * i, a1 = 3 * i + 1, a2 = 3 * i + 2;
+      r[i] = fmaxf(fmaxf(sacc[a0 >> 4][a0 & 15], sacc[a1 >> 4][a1 & 15]), sacc[a2 >> 4][a2 & 15]);
+    }
+    r[10] = fmaxf(sacc[1][14], sacc[1][15]);
+    const float r0 = fmaxf(fmaxf(r[0], r[1]), r[2]), r1 = fmaxf(fmaxf(r[3], r[4]), r[5]);
+    const float r2 = fmaxf(fmaxf(r[6], r[7]), r[8]), r3 = fmaxf(r[9], r[10]);
+    const float mx = pair_max32(fmaxf(fmaxf(r0, r1), fmaxf(r2, r3)));
+    // Lazy rescale: m moves only when some lane's max exceeds it by 2^8
+    // (always on the first tile).  Lanes whose max did not grow keep m.
+    if (first_tile || __any(mx > kRescale)) {
+      const float up = first_tile ? mx : fmaxf(mx, 0.f);
+      if (!first_tile) {
+        const float alpha = __builtin_amdgcn_exp2f(-up);
+        l_run *= alpha;
 #pragma unroll
-      for (int i = 0; i < DT; ++i) oacc[i] *= alpha;
+        for (int i = 0; i < DT; ++i) oacc[i] *= alpha;
+      }
+      first_tile = false;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        sacc[0][v] -= up;
+        sacc[1][v] -= up;
+        moff[v] -= up;
+      }
     }
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
       for (int v = 0; v < 16; ++v)
-        pf[t2][v >> 3][v & 7] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t2][v], c, -m_run)));
+        pf[t2][v >> 3][v & 7] = static_cast<__bf16>(__builtin_amdgcn_exp2f(sacc[t2][v]));
     // row sum of the rounded P (exactly what the PV product uses)
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2)
