@@ -36,7 +36,8 @@
 //   * Online softmax in base 2.  The Q fragments carry the scale and the QK
 //     accumulators start from minus the running max, so the product is
 //     already the exponent of P.  O and l are rescaled only when a row max
-//     grows by more than 2^8.
+//     grows by more than 2^8.  The row sum of P(t-1) is taken in the MFMA
+//     cluster of tile t, where the wave's VALU slots are otherwise idle.
 //
 // fp32 instance (head_dim <= 128, % 4): a plain tiled kernel (4 lanes per
 // query, 32-key LDS tiles, fp32 FMA), used for fp32 rounds.
@@ -268,6 +269,18 @@ __global__ __launch_bounds__(512, 1) void wf_attention_bf16_kernel(const AttnArg
         sacc[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qf[s], s == 0 ? moff : sacc[t2], 0, 0, 0);
       }
     }
+    // Row sum of P(t-1), the same rounded weights the PV product uses, in
+    // the VALU slots between this wave's MFMAs (it is added before the
+    // softmax of tile t can rescale l).
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int a2 = 0; a2 < 2; ++a2)
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const bf16x2 pp = {pf[t2][a2][e], pf[t2][a2][e + 1]};
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_run, false);
+        }
     // order: kAhead LDS reads, then (MFMA, LDS read) pairs, then MFMAs
     __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
 #pragma unroll
@@ -321,16 +334,6 @@ __global__ __launch_bounds__(512, 1) void wf_attention_bf16_kernel(const AttnArg
 #pragma unroll
       for (int v = 0; v < 16; ++v)
         pf[t2][v >> 3][v & 7] = static_cast<__bf16>(__builtin_amdgcn_exp2f(sacc[t2][v]));
-    // row sum of the rounded P (exactly what the PV product uses)
-#pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-      for (int a2 = 0; a2 < 2; ++a2)
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const bf16x2 pp = {pf[t2][a2][e], pf[t2][a2][e + 1]};
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_run, false);
-        }
   };
 
   // ---- prologue: tiles 0..2 into stages 0..2.  The first MFMA cluster
