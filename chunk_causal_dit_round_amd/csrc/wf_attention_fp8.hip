@@ -10,8 +10,9 @@
 //
 // CDNA4 v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x E4M3, fp32 accumulate):
 //   * the matrix core applies the scales: per query column the row exponent
-//     of Q (quantised here from the bf16 q_rot row), per tile the K or V
-//     exponent, so S and O come out in true units;
+//     of Q (quantised here from the bf16 q_rot row times scale * log2(e)),
+//     per tile the K or V exponent, so S comes out in base-2 exponent units
+//     and O in true units;
 //   * a lane holds 32 bytes of an operand; the product pairs byte j of lane
 //     half h of A with byte j of lane half h of B, so any k order works as
 //     long as both operands use the same one;
@@ -27,8 +28,10 @@
 // waves of a SIMD drift between clusters measured faster than the bf16
 // instance's ping-pong between wave groups.  K and Vt tiles live in a
 // 4-stage LDS ring with 16-byte chunks XOR-swizzled per row (conflict-free
-// operand reads and stores).  Softmax in base 2 with lazy rescale; the
-// weights, biased by 2^7, are rounded to E4M3 (at most 2^8 < 448).  The row
+// operand reads and stores).  Softmax in base 2 with lazy rescale; the QK
+// accumulators start from 2^7 divided by the running max (in exponent
+// units), so the weights come out of one exp2 per score already biased by
+// 2^7 and are rounded to E4M3 (at most 2^8 < 448).  The row
 // sum is one more FP8 MFMA of an all-ones operand against the same rounded
 // weights, so numerator and denominator use identical weights (and the
 // VALU, the bottleneck here, does no per-weight addition).
@@ -142,17 +145,20 @@ __global__ __launch_bounds__(kNT, 1) void wf_attention_fp8_kernel(const AttnArgs
   const int qc = q < N ? q : N - 1;
   const __bf16* qrow = static_cast<const __bf16*>(a.q_rot) +
                        ((static_cast<int64_t>(G.stage) * N + qc) * H + h) * kD;
+  // The row is multiplied by c = scale * log2(e) (fp32) before it is
+  // quantised, so S comes out in base-2 exponent units.
+  const float c = a.scale_log2e;
   float qv[2][32];
   float qmax = 0.f;
 #pragma unroll
   for (int s = 0; s < 2; ++s)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const bf16x8 x = *reinterpret_cast<const bf16x8*>(qrow + 64 * s + 32 * half + 8 * c);
+    for (int cc = 0; cc < 4; ++cc) {
+      const bf16x8 x = *reinterpret_cast<const bf16x8*>(qrow + 64 * s + 32 * half + 8 * cc);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        qv[s][8 * c + e] = static_cast<float>(x[e]);
-        qmax = fmaxf(qmax, fabsf(qv[s][8 * c + e]));
+        qv[s][8 * cc + e] = static_cast<float>(x[e]) * c;
+        qmax = fmaxf(qmax, fabsf(qv[s][8 * cc + e]));
       }
     }
   const int eq = fp8_exponent(pair_max32(qmax));
@@ -215,9 +221,10 @@ __global__ __launch_bounds__(kNT, 1) void wf_attention_fp8_kernel(const AttnArgs
   i32x8 ones;
 #pragma unroll
   for (int w = 0; w < 8; ++w) ones[w] = 0x38383838;   // E4M3 1.0
-  float m_run = -__builtin_inff();
-  float mb = -__builtin_inff();                   // kBias - m_run
-  const float c = a.scale_log2e;
+  // The QK accumulators start from moff = kBias - m (m = this lane's running
+  // max), so they hold S - m + kBias and P' = exp2(S) needs no per-score op.
+  f32x16 moff = f32x16{};
+  bool first_tile = true;
   int kcode = kE8M0One, vcode = kE8M0One;         // scales of the tiles in use
 
   // ---- MFMA cluster: O^T += Vt(t-1) P(t-1)^T, then S^T(t) = K(t) Q^T ----
@@ -262,7 +269,7 @@ __global__ __launch_bounds__(kNT, 1) void wf_attention_fp8_kernel(const AttnArgs
                                                                  kE8M0One);
       } else {
         const int j = i - 4, s = j >> 1, t2 = j & 1;
-        sacc[t2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f, qf[s], s == 0 ? f32x16{} : sacc[t2],
+        sacc[t2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f, qf[s], s == 0 ? moff : sacc[t2],
                                                                    0, 0, 0, kcode, 0, qscale);
       }
     }
@@ -285,24 +292,41 @@ __global__ __launch_bounds__(kNT, 1) void wf_attention_fp8_kernel(const AttnArgs
         for (int v = 0; v < 16; ++v)
           if (32 * half + 16 * t2 + v >= valid) sacc[t2][v] = -__builtin_inff();
     }
-    float mx = fmaxf(sacc[0][0], sacc[1][0]);
+    // max of the lane's 32 values (S - m + kBias) as a tree of 3-input maxima
+    float r[11];
 #pragma unroll
-    for (int v = 1; v < 16; ++v) mx = fmaxf(mx, fmaxf(sacc[0][v], sacc[1][v]));
-    mx = pair_max32(mx) * c;
-    if (__any(mx > m_run + kRescale)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      mb = kBias - m_new;
-      lacc *= alpha;
+    for (int i = 0; i < 10; ++i) {
+      const int a0 = 3 * i, a1 = 3 * i + 1, a2 = 3 * i + 2;
+      r[i] = fmaxf(fmaxf(sacc[a0 >> 4][a0 & 15], sacc[a1 >> 4][a1 & 15]), sacc[a2 >> 4][a2 & 15]);
+    }
+    r[10] = fmaxf(sacc[1][14], sacc[1][15]);
+    const float r0 = fmaxf(fmaxf(r[0], r[1]), r[2]), r1 = fmaxf(fmaxf(r[3], r[4]), r[5]);
+    const float r2 = fmaxf(fmaxf(r[6], r[7]), r[8]), r3 = fmaxf(r[9], r[10]);
+    const float mx = pair_max32(fmaxf(fmaxf(r0, r1), fmaxf(r2, r3))) - kBias;   // max S - m
+    // Lazy rescale: m moves only when some lane's max exceeds it by more
+    // than 2^kRescale (always on the first tile).
+    if (first_tile || __any(mx > kRescale)) {
+      const float up = first_tile ? mx : fmaxf(mx, 0.f);
+      if (!first_tile) {
+        const float alpha = __builtin_amdgcn_exp2f(-up);
+        lacc *= alpha;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) oacc[i] *= alpha;
+        for (int i = 0; i < 4; ++i) oacc[i] *= alpha;
+      }
+      // (before the first tile the accumulators start from 0, i.e. m = kBias)
+      first_tile = false;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        sacc[0][v] -= up;
+        sacc[1][v] -= up;
+        moff[v] -= up;
+      }
     }
     float p[2][16];
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) p[t2][v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t2][v], c, mb));
+      for (int v = 0; v < 16; ++v) p[t2][v] = __builtin_amdgcn_exp2f(sacc[t2][v]);
     // byte j = 16 t2 + v of the PV B operand
 #pragma unroll
     for (int w = 0; w < 8; ++w) {

@@ -61,9 +61,10 @@
  *                         nearest even; e is the smallest integer with
  *                         amax(tile) <= 448 * 2^e (0 for an all-zero tile).
  *                         Tokens N..Npad-1 are zero and never attended.
- *                         Attention quantises each bf16 q_rot row the same
- *                         way (one exponent per row) and multiplies on the
- *                         FP8 matrix cores; the softmax weights are
+ *                         Attention quantises each bf16 q_rot row times
+ *                         c = scale * log2(e) (fp32 product) the same way
+ *                         (one exponent per row) and multiplies on the FP8
+ *                         matrix cores; the softmax weights are
  *                         rounded to E4M3 for the PV product and the row
  *                         sum adds the same rounded weights.
  */

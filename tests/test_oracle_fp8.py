@@ -169,9 +169,31 @@ def test_fp8_round_reduces_to_dense_attention_on_dequantised_inputs():
         ks.append(F.fp8_tiles(kr))
         vs.append(F.fp8_tiles(raw(rnd, 0, cell, "v")[:, 1, :]))
     q = rope3d(raw(k, 0, stage, "q"), 3 * (k - stage), 3, 4, 6, cfg.rope_theta)[:, 1, :]
-    q = F.fp8_rows(F.bf16_round(q))
+    q = F.fp8_query(F.bf16_round(q), 1 / math.sqrt(64))
     ref = attend(q, np.concatenate(ks), np.concatenate(vs), 1 / math.sqrt(64))
     assert np.allclose(got[:, 0, :], ref, rtol=0, atol=1e-12)
     # and the FP8 result stays close to the exact one (quantisation only)
     exact = R.group_output(cfg, k, stage, 0, raw, heads=[1])
     assert np.max(np.abs(got - exact)) < 0.1
+
+
+def test_query_reading_scales_before_quantising():
+    """fp8_query quantises the fp32 product q * c per row: when c is a power
+    of two it equals plain per-row quantisation; otherwise it is the
+    dequantised scaled row divided by c, within half an E4M3 ulp of q."""
+    rng = np.random.default_rng(31)
+    q = F.bf16_round(rng.standard_normal((6, 128)))
+    log2e = math.log2(math.e)
+    for k in (-3, 0, 2):                     # c = 2^k exactly
+        scale = 2.0 ** k / log2e
+        assert np.float32(scale * log2e) == np.float32(2.0 ** k)
+        assert np.array_equal(F.fp8_query(q, scale), F.fp8_rows(q))
+    scale = 1 / math.sqrt(128)
+    c = float(np.float32(scale * log2e))
+    got = F.fp8_query(q, scale)
+    ref = F.fp8_rows((q.astype(np.float32) * np.float32(c)).astype(np.float64)) / c
+    assert np.array_equal(got, ref)
+    # within half an E4M3 ulp (relative 2^-4) plus the subnormal step of the row
+    amax = np.max(np.abs(q * c), axis=1, keepdims=True)
+    e = np.array([[F.pow2_exponent(a)] for a in amax[:, 0]])
+    assert np.all(np.abs(got - q) <= np.abs(q) * 2.0 ** -4 + 2.0 ** (e - 10) / c + 1e-12)

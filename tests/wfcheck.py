@@ -252,7 +252,7 @@ def check_attention(ro, k, layer, rows=None, heads=None, stages=None, seed=0):
             kk, vv = WR.group_keys(oc, k, st, layer, ro.raw, hs, fp8=True)
             tol = np.empty_like(err)
             for hi, h in enumerate(hs):
-                q8 = F8.fp8_rows(F8.bf16_round(qr[:, h, :]))
+                q8 = F8.fp8_query(F8.bf16_round(qr[:, h, :]), WR.scale_of(oc))
                 tol[:, hi, :] = fp8_attention_tolerance(q8, kk[:, hi, :], vv[:, hi, :],
                                                         WR.scale_of(oc))
             ratio = (err / tol).max()
