@@ -62,7 +62,8 @@ def _fp8_page(x: np.ndarray) -> np.ndarray:
 def group_keys(cfg: P.Config, k: int, stage: int, layer: int, raw, heads=None, fp8=False):
     """Concatenated rotated keys and values of query stage ``stage``:
     ([N_k, H', d], [N_k, H', d]) in plan order (WF §3.1, Eq. 5).  With
-    ``fp8`` each page is the FP8 page of the App. C.6 reading."""
+    ``fp8`` each page is the FP8 page of the App. C.6 reading; with
+    ``fp8="k"`` only the keys are (8-bit QK^T tier, values exact)."""
     ks, vs = [], []
     for kind, chunk, _slot in P.key_entries(cfg, k, stage):
         rnd, cell, frame0 = entry_source(cfg, k, kind, chunk)
@@ -72,7 +73,9 @@ def group_keys(cfg: P.Config, k: int, stage: int, layer: int, raw, heads=None, f
             kr, vr = kr[:, heads, :], vr[:, heads, :]
         kr = rope3d(kr, frame0, cfg.F, cfg.Hh, cfg.Ww, cfg.rope_theta)
         if fp8:
-            kr, vr = _fp8_page(kr), _fp8_page(vr)
+            kr = _fp8_page(kr)
+            if fp8 != "k":
+                vr = _fp8_page(vr)
         ks.append(kr)
         vs.append(vr)
     return np.concatenate(ks, axis=0), np.concatenate(vs, axis=0)
@@ -90,8 +93,9 @@ def group_output(cfg: P.Config, k: int, stage: int, layer: int, raw,
 
     ``rows`` / ``heads`` select query tokens and heads (all by default);
     every selected row still attends to its full key list.  With ``fp8`` the
-    pages are FP8 pages and each rotated query row, stored in bf16, is
-    scaled and quantised per row (App. C.6 reading, ``wf_fp8.fp8_query``).
+    pages are FP8 pages (``fp8="k"``: FP8 keys, exact values) and each
+    rotated query row, stored in bf16, is scaled and quantised per row (App.
+    C.6 reading, ``wf_fp8.fp8_query``).
     """
     heads = list(range(cfg.n_heads)) if heads is None else list(heads)
     qr = q_rot(cfg, k, stage, layer, raw)

@@ -197,3 +197,42 @@ def test_query_reading_scales_before_quantising():
     amax = np.max(np.abs(q * c), axis=1, keepdims=True)
     e = np.array([[F.pow2_exponent(a)] for a in amax[:, 0]])
     assert np.all(np.abs(got - q) <= np.abs(q) * 2.0 ** -4 + 2.0 ** (e - 10) / c + 1e-12)
+
+
+def test_fp8_keys_only_round_is_dense_attention_with_exact_values():
+    """The 8-bit QK^T tier: keys quantised per 64-token tile, values exact,
+    queries by the FP8 query reading (a tiny config, one head)."""
+    from oracle import wf_plan as P
+    from oracle import wf_round as R
+    from oracle.wf_attention import attend
+    from oracle.wf_rope import rope3d
+
+    cfg = P.Config(S=2, W=2, W_store=4, anchor=1, n_chunk=6, F=3, Hh=4, Ww=6,
+                   n_heads=2, head_dim=64, n_layers=1, mask=0)
+    rng = np.random.default_rng(22)
+    cache = {}
+
+    def raw(rnd, layer, cell, name):
+        key = (rnd, layer, cell, name)
+        if key not in cache:
+            cache[key] = rng.standard_normal((72, 2, 64))
+        return cache[key]
+
+    k, stage = 5, 0
+    got = R.group_output(cfg, k, stage, 0, raw, heads=[0], fp8="k")
+    ks, vs = [], []
+    for kind, chunk, _slot in P.key_entries(cfg, k, stage):
+        rnd, cell, frame0 = R.entry_source(cfg, k, kind, chunk)
+        kr = rope3d(raw(rnd, 0, cell, "k"), frame0, 3, 4, 6, cfg.rope_theta)[:, 0, :]
+        ks.append(F.fp8_tiles(kr))
+        vs.append(raw(rnd, 0, cell, "v")[:, 0, :])
+    q = rope3d(raw(k, 0, stage, "q"), 3 * (k - stage), 3, 4, 6, cfg.rope_theta)[:, 0, :]
+    q = F.fp8_query(F.bf16_round(q), 1 / math.sqrt(64))
+    ref = attend(q, np.concatenate(ks), np.concatenate(vs), 1 / math.sqrt(64))
+    assert np.allclose(got[:, 0, :], ref, rtol=0, atol=1e-12)
+    # values untouched: the keys-only page differs from the full FP8 page
+    _, vv_k = R.group_keys(cfg, k, stage, 0, raw, [0], fp8="k")
+    _, vv = R.group_keys(cfg, k, stage, 0, raw, [0])
+    assert np.array_equal(vv_k, vv)
+    _, vv_kv = R.group_keys(cfg, k, stage, 0, raw, [0], fp8=True)
+    assert not np.array_equal(vv_kv, vv)
