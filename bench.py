@@ -23,6 +23,9 @@ Other modes (one JSON line each):
   --workload wan1.3b_4step_fp8
                      the same round over FP8 (E4M3) pages; roofline against the
                      dense fp8 MFMA peak.
+  --workload wan1.3b_4step_fp8k
+                     the same round over 8-bit-key pages (FP8 keys, bf16 values);
+                     roofline against the blend of the fp8 and bf16 peaks.
   --dit              the whole DiT forward of a steady round: every layer of the
                      Wan-shaped block (norms, QKV / output / FFN products, qk norm,
                      publish, attention) for all S+1 cells, dummy weights, FFN
@@ -44,17 +47,38 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
+# 8-bit-key pages: half the attention FLOPs (Q K^T) on the fp8 matrix cores,
+# half (P V) on the bf16 ones; at both peaks a launch takes F/2/5.0 + F/2/2.5,
+# so its peak is the harmonic blend, 3.33 PFLOP/s.
+PEAK_FP8K_TFLOPS = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
 PEAK_HBM_GBPS = 8000.0
-ATTN_SRC = os.path.join(ROOT, "chunk_causal_dit_round_amd", "csrc", "wf_attention.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_bf16_wan1.3b_4step_hbm_traffic.txt")
+CSRC = os.path.join(ROOT, "chunk_causal_dit_round_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+# Attention instance per page type: peak, dtype label, kernel, its source and
+# the committed counter summary its HBM traffic comes from.
+PAGE_KINDS = {
+    "bf16": dict(peak=PEAK_BF16_TFLOPS, dtype="bf16", kernel="wf_attention_bf16_kernel<128>",
+                 src="wf_attention.hip", traffic="attention_bf16_wan1.3b_4step_hbm_traffic.txt",
+                 what="bf16 MFMA peak"),
+    "fp8": dict(peak=PEAK_FP8_TFLOPS, dtype="fp8", kernel="wf_attention_fp8_kernel",
+                src="wf_attention_fp8.hip",
+                traffic="attention_fp8_wan1.3b_4step_kernel_trace_and_traffic.txt",
+                what="fp8 MFMA peak (FP8 E4M3 pages)"),
+    "fp8k": dict(peak=PEAK_FP8K_TFLOPS, dtype="fp8 QK^T + bf16 PV", kernel="wf_attention_fp8k_kernel",
+                 src="wf_attention_fp8k.hip",
+                 traffic="attention_fp8k_wan1.3b_4step_kernel_trace_and_traffic.txt",
+                 what="blended fp8 / bf16 MFMA peak (8-bit-key pages: FP8 K, bf16 V)"),
+}
 
 
-def measured_traffic():
+def measured_traffic(kind):
     """HBM bytes per attention launch from the committed counter summary, or
     None if the kernel source changed since the counters were taken."""
     try:
-        fields = dict(line.split(":", 1) for line in open(TRAFFIC_FILE) if ":" in line)
-        src = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+        fields = dict(line.split(":", 1) for line in open(os.path.join(PROFILES, kind["traffic"]))
+                      if ":" in line)
+        src = hashlib.sha256(open(os.path.join(CSRC, kind["src"]), "rb").read()).hexdigest()
         if fields.get("kernel_source_sha256", "").strip() != src:
             return None
         return float(fields["traffic_bytes_per_launch"])
@@ -405,13 +429,12 @@ def main():
     pub_bytes_launch = plans[0].publish_bytes / L
     achieved = flops_launch / (att_avg * 1e-3) / 1e12
     total_flops = sum(p.flops for p in plans)
-    fp8 = w.dtype == wf.WF_FP8
-    peak = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
+    kind = PAGE_KINDS[{wf.WF_FP8: "fp8", wf.WF_FP8K: "fp8k"}.get(w.dtype, "bf16")]
+    fp8 = {wf.WF_FP8: True, wf.WF_FP8K: "k"}.get(w.dtype, False)
+    peak = kind["peak"]
 
     res = {
-        "metric": ("wavefront rounds/sec (=chunks/sec) and attention TFLOP/s vs fp8 MFMA peak "
-                   "(FP8 E4M3 pages)" if fp8 else
-                   "wavefront rounds/sec (=chunks/sec) and attention TFLOP/s vs bf16 MFMA peak"),
+        "metric": "wavefront rounds/sec (=chunks/sec) and attention TFLOP/s vs " + kind["what"],
         "value": args.steps / elapsed,
         "unit": "rounds/s",
         "n_gpus": 1,
@@ -421,7 +444,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8" if fp8 else "bf16",
+        "dtype": kind["dtype"],
         "data": "synthetic",
         "config": {"workload": f"{w.name} steady wavefront round", "S": w.S, "W": w.W,
                    "W_store": w_store, "anchor": w.anchor, "n_chunk": w.n_chunk,
@@ -430,8 +453,8 @@ def main():
                    "rounds_timed": [k0, k0 + args.steps - 1], "n_rounds": n_rounds},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak,
                      "unit": "TFLOP/s", "frac": achieved / peak,
-                     "traffic": None if fp8 else measured_traffic(),
-                     "kernel": "wf_attention_fp8_kernel" if fp8 else "wf_attention_bf16_kernel<128>",
+                     "traffic": measured_traffic(kind),
+                     "kernel": kind["kernel"],
                      "flops_per_launch": flops_launch, "avg_launch_ms": att_avg},
         "attention_tflops_round": total_flops / elapsed / 1e12,
         "publish": {"avg_launch_ms": pub_avg, "bytes_per_launch": pub_bytes_launch,

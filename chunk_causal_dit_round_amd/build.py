@@ -18,11 +18,12 @@ LIB = os.path.join(PKG, "libwf.so")
 ARCH = "gfx950"
 
 HIP_SOURCES = ["wf_runtime.cpp", "wf_publish.hip", "wf_attention.hip", "wf_attention_fp8.hip",
-               "wf_dit.hip", "wf_dit.cpp"]
+               "wf_attention_fp8k.hip", "wf_dit.hip", "wf_dit.cpp"]
 # Attention scores are finite or -inf, never NaN: without NaN semantics the
 # row max needs no canonicalising v_max x,x per score.
 FILE_FLAGS = {"wf_attention.hip": ["-fno-honor-nans"],
-              "wf_attention_fp8.hip": ["-fno-honor-nans"]}
+              "wf_attention_fp8.hip": ["-fno-honor-nans"],
+              "wf_attention_fp8k.hip": ["-fno-honor-nans"]}
 CXX_SOURCES = ["wf_plan.cpp"]
 
 # Packed fp32 VALU forms are switched off for all device code.

@@ -70,12 +70,14 @@ struct AttnArgs {
 // Query rows per work item of each attention instance.
 constexpr int kAttnBM_bf16 = 256;
 constexpr int kAttnBM_fp8 = 256;
+constexpr int kAttnBM_fp8k = 256;
 constexpr int kAttnBM_f32 = 64;
-// FP8 attention keeps the scale codes of a group's whole context in LDS.
+// FP8 / FP8K attention keeps the scale codes of a group's whole context in LDS.
 constexpr int kFp8MaxCtxTiles = 4096;
 
 hipError_t launch_publish(const PublishArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_attention(const AttnArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_attention_fp8(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_attention_fp8k(const AttnArgs& a, hipStream_t stream);
 
 }  // namespace wf

@@ -35,8 +35,8 @@ bool derive_shape(const wf_config* c, Shape* o, std::string* why) {
   if (c->head_dim < 6 || c->head_dim > 512 || (c->head_dim & 1))
     return fail(why, "head_dim must be even and in [6, 512]");
   if (c->n_layers < 1 || c->n_layers > 4096) return fail(why, "n_layers must be in [1, 4096]");
-  if (c->dtype != WF_F32 && c->dtype != WF_BF16 && c->dtype != WF_FP8)
-    return fail(why, "dtype must be WF_F32, WF_BF16 or WF_FP8");
+  if (c->dtype != WF_F32 && c->dtype != WF_BF16 && c->dtype != WF_FP8 && c->dtype != WF_FP8K)
+    return fail(why, "dtype must be WF_F32, WF_BF16, WF_FP8 or WF_FP8K");
   if (c->mask != WF_MASK_WAVE && c->mask != WF_MASK_ROLLING)
     return fail(why, "mask must be WF_MASK_WAVE or WF_MASK_ROLLING");
   if (c->reserved != 0) return fail(why, "reserved must be 0");
@@ -81,9 +81,11 @@ bool derive_shape(const wf_config* c, Shape* o, std::string* why) {
     return fail(why, "page size overflows");
   s.page_elems = pe;
   if (!mul_ok(pe, s.elem, &s.anchor_page_bytes)) return fail(why, "page size overflows");
-  if (c->dtype == WF_FP8) {
+  if (c->dtype == WF_FP8 || c->dtype == WF_FP8K) {
+    // K in one byte per element; V in one (FP8) or two (FP8K: bf16) bytes
     size_t kv = 0;
-    if (!mul_ok(size_t(2) * s.H, size_t(s.Npad), &kv) || !mul_ok(kv, size_t(s.D), &kv))
+    const size_t bytes_kv = c->dtype == WF_FP8 ? 2 : 3;
+    if (!mul_ok(bytes_kv * s.H, size_t(s.Npad), &kv) || !mul_ok(kv, size_t(s.D), &kv))
       return fail(why, "page size overflows");
     const size_t codes = size_t(2) * s.H * s.T;
     s.page_bytes = (kv + codes + 255) / 256 * 256;
@@ -202,6 +204,10 @@ void build_plan(const Shape& sh, uint64_t hash, int64_t k, wf_plan* p) {
     // K, Vt shrink to 1 byte; the anchor slot write shrinks likewise
     per_layer -= 2.0 * p->n_active * nhd;
     if (p->anchor.present) per_layer -= 2.0 * nhd;
+  } else if (sh.dtype == WF_FP8K) {
+    // only K shrinks to 1 byte
+    per_layer -= 1.0 * p->n_active * nhd;
+    if (p->anchor.present) per_layer -= 1.0 * nhd;
   }
   p->publish_bytes = double(sh.L) * per_layer;
 }

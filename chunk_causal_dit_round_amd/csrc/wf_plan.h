@@ -28,15 +28,18 @@ struct Shape {
   size_t page_elems;           // 2 H N D
   // Pool page in bytes.  fp32 / bf16: page_elems * elem.  FP8: K [H][Npad][D]
   // and Vt [H][D][Npad] in E4M3, then the per-tile scale codes [H][T][2],
-  // rounded up to 256 bytes (Npad = 64 T >= N).
+  // rounded up to 256 bytes (Npad = 64 T >= N).  FP8K: the same with Vt in
+  // bf16.
   size_t page_bytes;
   size_t anchor_page_bytes;    // raw K + Vt of chunk 0 (bf16 for FP8 pages)
   int Npad, T;
 };
 
-// FP8 page sections (byte offsets inside a page).
+// FP8 / FP8K page sections (byte offsets inside a page).
 inline size_t fp8_v_offset(const Shape& sh) { return size_t(sh.H) * sh.Npad * sh.D; }
-inline size_t fp8_code_offset(const Shape& sh) { return 2 * size_t(sh.H) * sh.Npad * sh.D; }
+inline size_t fp8_code_offset(const Shape& sh) {
+  return size_t(sh.dtype == WF_FP8K ? 3 : 2) * sh.H * sh.Npad * sh.D;
+}
 
 // Validates cfg (method-level rules only) and fills `out`.  Returns false
 // with a reason in `why` when the config is invalid.

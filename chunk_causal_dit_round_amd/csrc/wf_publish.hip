@@ -160,6 +160,8 @@ __global__ __launch_bounds__(kThreads) void wf_publish_kernel(const PublishArgs 
 // get one power-of-two scale 2^e with e the smallest integer such that
 // amax(tile) <= 448 * 2^e, and are stored as OCP E4M3 codes of x / 2^e
 // (round to nearest even).  q_rot stays bf16.  Tokens N..Npad-1 are zero.
+// With kBf16V (the 8-bit QK^T tier) only K is quantised; Vt is written in
+// bf16 (its scale code stays 2^0).
 constexpr int kFp8D = 128;
 constexpr int kFp8Items = kTokens * (kFp8D / 8) / kThreads;   // (row, 8-dim chunk) per thread
 
@@ -214,6 +216,7 @@ __device__ inline float wave_max(float v) {
   return v;
 }
 
+template <bool kBf16V>
 __global__ __launch_bounds__(kThreads) void wf_publish_fp8_kernel(const PublishArgs a) {
   // V tile staged token-major in fp32 for the amax and the transposed write.
   __shared__ float vtile[kTokens][kFp8D + 1];
@@ -228,8 +231,8 @@ __global__ __launch_bounds__(kThreads) void wf_publish_fp8_kernel(const PublishA
   const int tid = threadIdx.x;
   uint8_t* page = static_cast<uint8_t*>(a.pool) + static_cast<int64_t>(task.slot) * a.page_bytes;
   uint8_t* K8 = page;                                             // [H][Np][D]
-  uint8_t* V8 = page + static_cast<int64_t>(H) * Np * D;          // [H][D][Np]
-  uint8_t* codes = page + 2 * static_cast<int64_t>(H) * Np * D;   // [H][T][2]
+  uint8_t* V8 = page + static_cast<int64_t>(H) * Np * D;          // [H][D][Np] (bf16 with kBf16V)
+  uint8_t* codes = page + (kBf16V ? 3 : 2) * static_cast<int64_t>(H) * Np * D;   // [H][T][2]
   const int64_t hnd = static_cast<int64_t>(H) * N * D;
   __bf16* ancK = static_cast<__bf16*>(a.anchor_raw);              // bf16 [H][N][D]
   __bf16* ancVt = ancK + hnd;                                     // bf16 [H][D][N]
@@ -318,7 +321,7 @@ __global__ __launch_bounds__(kThreads) void wf_publish_fp8_kernel(const PublishA
     kmax = fmaxf(kmax, red[0][w]);
     vmax = fmaxf(vmax, red[1][w]);
   }
-  const int ek = fp8_exponent(kmax), ev = fp8_exponent(vmax);
+  const int ek = fp8_exponent(kmax), ev = kBf16V ? 0 : fp8_exponent(vmax);
   const float sk = ldexpf(1.f, -ek), sv = ldexpf(1.f, -ev);
 
   // K rows: 8 codes per (row, chunk); padding rows are zero codes
@@ -334,11 +337,18 @@ __global__ __launch_bounds__(kThreads) void wf_publish_fp8_kernel(const PublishA
 #pragma unroll
   for (int i = 0; i < kFp8Items; ++i) {
     const int idx = tid + i * kThreads, d = idx >> 3, g = idx & 7;
-    float x[8];
+    if (kBf16V) {
+      bf16x8 o;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = vtile[8 * g + e][d] * sv;
-    const uint2 o = fp8_pack8(x);
-    *reinterpret_cast<uint2*>(V8 + (static_cast<int64_t>(h) * D + d) * Np + tok0 + 8 * g) = o;
+      for (int e = 0; e < 8; ++e) o[e] = static_cast<__bf16>(vtile[8 * g + e][d]);
+      *reinterpret_cast<bf16x8*>(reinterpret_cast<__bf16*>(V8) + (static_cast<int64_t>(h) * D + d) * Np + tok0 + 8 * g) = o;
+    } else {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = vtile[8 * g + e][d] * sv;
+      const uint2 o = fp8_pack8(x);
+      *reinterpret_cast<uint2*>(V8 + (static_cast<int64_t>(h) * D + d) * Np + tok0 + 8 * g) = o;
+    }
     if (task.mode == TASK_CAPTURE && tok0 + 8 * g < N) {
       bf16x8 raw;
 #pragma unroll
@@ -356,9 +366,10 @@ __global__ __launch_bounds__(kThreads) void wf_publish_fp8_kernel(const PublishA
 
 hipError_t launch_publish(const PublishArgs& a, int dtype, hipStream_t stream) {
   if (a.n_tasks <= 0) return hipSuccess;
-  if (dtype == WF_FP8) {
+  if (dtype == WF_FP8 || dtype == WF_FP8K) {
     const dim3 grid(a.T, a.H, a.n_tasks);
-    hipLaunchKernelGGL(wf_publish_fp8_kernel, grid, dim3(kThreads), 0, stream, a);
+    if (dtype == WF_FP8) hipLaunchKernelGGL(wf_publish_fp8_kernel<false>, grid, dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL(wf_publish_fp8_kernel<true>, grid, dim3(kThreads), 0, stream, a);
     return hipGetLastError();
   }
   const dim3 grid((a.N + kTokens - 1) / kTokens, a.H, a.n_tasks);

@@ -46,14 +46,16 @@ wf_status check_supported(const wf::Shape& sh) {
     // Attention addresses a layer's slots with 32-bit byte offsets.
     if (double(sh.n_slots) * double(sh.page_elems) * 2.0 >= 4294967296.0)
       return fail(WF_EUNSUPPORTED, "bf16 kernels need one layer's slot pool below 4 GiB");
-  } else if (sh.dtype == WF_FP8) {
-    if (sh.D != 128) return fail(WF_EUNSUPPORTED, "FP8 kernels need head_dim 128");
-    if (sh.N % 8 != 0) return fail(WF_EUNSUPPORTED, "FP8 kernels need tokens per chunk % 8 == 0");
+  } else if (sh.dtype == WF_FP8 || sh.dtype == WF_FP8K) {
+    const char* name = sh.dtype == WF_FP8 ? "FP8" : "FP8K";
+    if (sh.D != 128) return fail(WF_EUNSUPPORTED, std::string(name) + " kernels need head_dim 128");
+    if (sh.N % 8 != 0) return fail(WF_EUNSUPPORTED, std::string(name) + " kernels need tokens per chunk % 8 == 0");
     if (double(sh.n_slots) * double(sh.page_bytes) >= 4294967296.0)
-      return fail(WF_EUNSUPPORTED, "FP8 kernels need one layer's slot pool below 4 GiB");
+      return fail(WF_EUNSUPPORTED, std::string(name) + " kernels need one layer's slot pool below 4 GiB");
     const int worst = 1 + sh.Wmax + 1 + sh.S;
     if (worst * sh.T > wf::kFp8MaxCtxTiles)
-      return fail(WF_EUNSUPPORTED, "FP8 attention needs (longest context pages) * ceil(N/64) <= 4096");
+      return fail(WF_EUNSUPPORTED,
+                  std::string(name) + " attention needs (longest context pages) * ceil(N/64) <= 4096");
   } else {
     if (sh.D % 4 != 0 || sh.D > 128)
       return fail(WF_EUNSUPPORTED, "fp32 kernels need head_dim % 4 == 0 and <= 128");
@@ -140,9 +142,10 @@ wf_status do_attention(wf_handle* h, const wf_plan& p, int layer, const void* q_
   a.H = sh.H;
   a.D = sh.D;
   a.scale_log2e = static_cast<float>(sh.scale * 1.4426950408889634);
-  const int bm = sh.dtype == WF_BF16 ? wf::kAttnBM_bf16
-                 : sh.dtype == WF_FP8 ? wf::kAttnBM_fp8
-                                      : wf::kAttnBM_f32;
+  const int bm = sh.dtype == WF_BF16  ? wf::kAttnBM_bf16
+                 : sh.dtype == WF_FP8  ? wf::kAttnBM_fp8
+                 : sh.dtype == WF_FP8K ? wf::kAttnBM_fp8k
+                                       : wf::kAttnBM_f32;
   a.q_tiles = (sh.N + bm - 1) / bm;
   // Active groups, longest context first (ties: lower stage first).
   int order[WF_MAX_GROUPS];
@@ -164,8 +167,9 @@ wf_status do_attention(wf_handle* h, const wf_plan& p, int layer, const void* q_
   a.n_groups = ng;
   a.n_items = item;
   (void)hipGetLastError();
-  const hipError_t e = sh.dtype == WF_FP8 ? wf::launch_attention_fp8(a, stream)
-                                           : wf::launch_attention(a, sh.dtype, stream);
+  const hipError_t e = sh.dtype == WF_FP8    ? wf::launch_attention_fp8(a, stream)
+                       : sh.dtype == WF_FP8K ? wf::launch_attention_fp8k(a, stream)
+                                             : wf::launch_attention(a, sh.dtype, stream);
   if (e != hipSuccess) return fail(WF_EDEVICE, std::string("attention launch: ") + hipGetErrorString(e));
   return ok();
 }

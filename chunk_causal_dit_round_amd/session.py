@@ -9,8 +9,9 @@ import torch
 
 from . import wf
 
-# q/k/v/q_rot/out and anchor_raw element type; FP8 configs keep them bf16
-TORCH_DTYPE = {wf.WF_F32: torch.float32, wf.WF_BF16: torch.bfloat16, wf.WF_FP8: torch.bfloat16}
+# q/k/v/q_rot/out and anchor_raw element type; FP8 and FP8K configs keep them bf16
+TORCH_DTYPE = {wf.WF_F32: torch.float32, wf.WF_BF16: torch.bfloat16, wf.WF_FP8: torch.bfloat16,
+               wf.WF_FP8K: torch.bfloat16}
 
 
 class Session:
@@ -47,13 +48,17 @@ class Session:
         return p[:hnd].view(self.H, self.N, self.D), p[hnd:].view(self.H, self.D, self.N)
 
     def fp8_page(self, layer: int, slot: int):
-        """(K8 [H][Npad][D], Vt8 [H][D][Npad], codes [H][T][2]) uint8 views of
-        one slot of an FP8 pool (codes: exponent + 127 of K, V per tile)."""
+        """(K8 [H][Npad][D], Vt [H][D][Npad], codes [H][T][2]) views of one
+        slot of an FP8 or FP8K pool (codes: exponent + 127 of K, V per tile).
+        K8 and codes are uint8; Vt is uint8 E4M3 codes (FP8) or bf16 (FP8K)."""
         H, D, Np, T = self.H, self.D, self.Npad, self.T
         p = self.pool.view(self.L, self.n_slots, self.page_bytes)[layer, slot]
         kv = H * Np * D
-        return (p[:kv].view(H, Np, D), p[kv:2 * kv].view(H, D, Np),
-                p[2 * kv:2 * kv + 2 * H * T].view(H, T, 2))
+        vb = 2 * kv if self.cfg.dtype == wf.WF_FP8K else kv
+        vt = p[kv:kv + vb]
+        vt = vt.view(torch.bfloat16) if self.cfg.dtype == wf.WF_FP8K else vt
+        return (p[:kv].view(H, Np, D), vt.view(H, D, Np),
+                p[kv + vb:kv + vb + 2 * H * T].view(H, T, 2))
 
     def anchor_page(self, layer: int):
         hnd = self.H * self.N * self.D

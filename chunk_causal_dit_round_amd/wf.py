@@ -16,7 +16,7 @@ WF_MAX_GROUPS = WF_MAX_STAGES + 1
 WF_MAX_PAGES = 48
 
 WF_OK, WF_EINVAL, WF_ERANGE, WF_EORDER, WF_ESMALL, WF_EDEVICE, WF_EUNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
-WF_F32, WF_BF16, WF_FP8 = 0, 1, 2
+WF_F32, WF_BF16, WF_FP8, WF_FP8K = 0, 1, 2, 3
 WF_MASK_WAVE, WF_MASK_ROLLING = 0, 1
 WF_KIND_ANCHOR, WF_KIND_HISTORY, WF_KIND_STORE, WF_KIND_DENOISE = 0, 1, 2, 3
 

@@ -59,6 +59,9 @@ WAN14B_4STEP = Workload("wan14b_4step", S=4, W=4, n_chunk=133, F=3, Hh=30, Ww=52
 
 # The same 1.3B round over FP8 (E4M3) pages (App. C.6 variant).
 WAN13B_4STEP_FP8 = WAN13B_4STEP.with_(name="wan1.3b_4step_fp8", dtype=wf.WF_FP8)
+# ... and over 8-bit-key pages (FP8 keys, bf16 values: the 8-bit QK^T tier of
+# App. B.1 / App. C.2 Tab. 4).
+WAN13B_4STEP_FP8K = WAN13B_4STEP.with_(name="wan1.3b_4step_fp8k", dtype=wf.WF_FP8K)
 
 ALL = {w.name: w for w in (TINY_FP32, WAN13B_4STEP, WAN13B_5STEP, WAN13B_5STEP_ROLLING,
-                           WAN14B_4STEP, WAN13B_4STEP_FP8)}
+                           WAN14B_4STEP, WAN13B_4STEP_FP8, WAN13B_4STEP_FP8K)}

@@ -67,6 +67,19 @@
  *                         matrix cores; the softmax weights are
  *                         rounded to E4M3 for the PV product and the row
  *                         sum adds the same rounded weights.
+ *
+ * 8-bit QK^T pages (dtype WF_FP8K; WF App. B.1 and App. C.2 Tab. 4: an
+ * approximate compute mode swaps self-attention for SageAttention, which
+ * multiplies Q K^T in 8 bits and P V in higher precision): the FP8 page
+ * layout with the values kept in bf16:
+ *                         K8  [H][Npad][D]  E4M3 codes of RoPE(k) / 2^eK
+ *                         Vt  [H][D][Npad]  bf16 values, keys padded with 0
+ *                         codes [H][T][2]   eK + 127, 127 (values unscaled)
+ *                         rounded up to 256 bytes.  Attention quantises the
+ *                         query rows as for FP8 pages and multiplies Q K^T on
+ *                         the FP8 matrix cores, P V on the bf16 matrix cores
+ *                         (softmax weights rounded to bf16, row sum of the
+ *                         same rounded weights).
  */
 #ifndef WF_H
 #define WF_H
@@ -96,7 +109,8 @@ typedef enum {
 typedef enum {
   WF_F32 = 0,   /* everything fp32                                           */
   WF_BF16 = 1,  /* everything bf16 (fp32 accumulation)                       */
-  WF_FP8 = 2    /* bf16 tensors, FP8 E4M3 pages (see "FP8 pages" above)      */
+  WF_FP8 = 2,   /* bf16 tensors, FP8 E4M3 pages (see "FP8 pages" above)      */
+  WF_FP8K = 3   /* bf16 tensors, FP8 keys and bf16 values (8-bit QK^T tier)  */
 } wf_dtype;
 
 typedef enum {

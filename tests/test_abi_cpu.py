@@ -13,7 +13,8 @@ import re
 import pytest
 
 from chunk_causal_dit_round_amd import wf
-from chunk_causal_dit_round_amd.workloads import ALL, TINY_FP32, WAN13B_4STEP, WAN13B_4STEP_FP8
+from chunk_causal_dit_round_amd.workloads import (ALL, TINY_FP32, WAN13B_4STEP, WAN13B_4STEP_FP8,
+                                                  WAN13B_4STEP_FP8K)
 from oracle import wf_plan as P
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -109,11 +110,36 @@ def test_plan_numbers_fp8():
     wf.wf_destroy(h)
 
 
+def test_pool_bytes_fp8k():
+    """8-bit-key pages: K8 [H][Npad][D] (1 byte) + Vt [H][D][Npad] (bf16) +
+    codes [H][T][2], rounded up to 256 bytes."""
+    cfg = WAN13B_4STEP_FP8K.config()
+    pool, anc, tab = wf.wf_pool_bytes(cfg)
+    T = 74
+    page = -(-(3 * 12 * 64 * T * 128 + 2 * 12 * T) // 256) * 256
+    assert pool == 30 * 20 * page
+    assert anc == 30 * 2 * 4680 * 12 * 128 * 2
+    assert tab == wf.wf_pool_bytes(WAN13B_4STEP.config())[2]
+
+
+def test_plan_numbers_fp8k():
+    """Same FLOPs as bf16; per cell q,k,v in + q_rot out (bf16), K out (1
+    byte) and Vt out (bf16); anchor: raw K, Vt in + K (1) and Vt (2) out."""
+    h = wf.wf_create(WAN13B_4STEP_FP8K.config())
+    p = wf.wf_round_plan(h, 13)
+    assert abs(p.flops - 1.7763e14) / 1.7763e14 < 1e-4
+    nhd = 4680 * 12 * 128
+    assert p.publish_bytes == 30 * (5 * 11 + 7) * nhd
+    wf.wf_destroy(h)
+
+
 def test_fp8_unsupported_shapes():
     fake = 1 << 20
     for w in (WAN13B_4STEP_FP8.with_(head_dim=64), WAN13B_4STEP_FP8.with_(Ww=51),
               # longest context 40 pages x 104 tiles > 4096 tiles
-              WAN13B_4STEP_FP8.with_(W=30, Hh=40, Ww=55)):
+              WAN13B_4STEP_FP8.with_(W=30, Hh=40, Ww=55),
+              WAN13B_4STEP_FP8K.with_(head_dim=64), WAN13B_4STEP_FP8K.with_(Ww=51),
+              WAN13B_4STEP_FP8K.with_(W=30, Hh=40, Ww=55)):
         cfg = w.config()
         h = wf.wf_create(cfg)
         pb, ab, tb = wf.wf_pool_bytes(cfg)

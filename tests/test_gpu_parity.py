@@ -6,8 +6,10 @@ anchor re-rotation, ring wrap).  Full Wan2.1 shapes are compared on sampled
 query rows (each against its full key list) and on whole pages.
 
 Tolerances: attention max-abs error 2e-2 for bf16 inputs, 1e-4 for fp32
-inputs; RoPE'd q/k within one bf16 unit in the last place (fp32: 2e-6
-relative); values and every plan field bit-exact.
+inputs; over FP8 and 8-bit-key pages the per-element bound derived in
+``wfcheck.fp8_attention_tolerance`` from the rounding of the softmax
+weights; RoPE'd q/k within one bf16 unit in the last place (fp32: 2e-6
+relative); values, codes, exponents and every plan field bit-exact.
 """
 
 import gc
@@ -17,7 +19,7 @@ import torch
 
 from chunk_causal_dit_round_amd import wf
 from chunk_causal_dit_round_amd.workloads import (TINY_FP32, WAN13B_4STEP, WAN13B_4STEP_FP8,
-                                                  WAN13B_5STEP, WAN13B_5STEP_ROLLING,
+                                                  WAN13B_4STEP_FP8K, WAN13B_5STEP, WAN13B_5STEP_ROLLING,
                                                   WAN14B_4STEP, Workload)
 from wfcheck import Rollout, check_attention, check_publish
 
@@ -193,5 +195,57 @@ def test_full_size_wan14b_4step_sampled():
             ro.run(k)
         err = check_attention(ro, 14, w.n_layers - 1, rows=32)
         _log(f"  k=14 layer={w.n_layers - 1} max abs err {err:.3e}")
+    finally:
+        ro.close()
+
+
+SMALL_FP8K = [
+    # 8-bit-key pages (FP8 keys, bf16 values): the FP8 shapes' edge cases
+    Workload("fp8k_s4_n360", S=4, W=4, n_chunk=12, F=3, Hh=10, Ww=12, n_heads=3,
+             head_dim=128, n_layers=2, dtype=wf.WF_FP8K),
+    Workload("fp8k_s2_n128", S=2, W=2, n_chunk=8, F=2, Hh=8, Ww=8, n_heads=2,
+             head_dim=128, n_layers=1, dtype=wf.WF_FP8K),
+    Workload("fp8k_s2_n72", S=2, W=2, n_chunk=8, F=3, Hh=4, Ww=6, n_heads=2,
+             head_dim=128, n_layers=1, dtype=wf.WF_FP8K),
+    Workload("fp8k_rolling_n64", S=3, W=2, n_chunk=7, F=1, Hh=8, Ww=8, n_heads=2,
+             head_dim=128, n_layers=1, mask=wf.WF_MASK_ROLLING, dtype=wf.WF_FP8K),
+    Workload("fp8k_headscale", S=2, W=3, anchor=0, n_chunk=7, F=1, Hh=16, Ww=16, n_heads=4,
+             head_dim=128, n_layers=1, q_head_scale=True, dtype=wf.WF_FP8K),
+]
+
+
+@pytest.mark.parametrize("w", SMALL_FP8K, ids=lambda w: w.name)
+def test_small_fp8k_every_round(w):
+    _log(f"{w.name}: {w.n_chunk + w.S} rounds")
+    ro = Rollout(w)
+    worst = 0.0
+    try:
+        for k in range(w.n_chunk + w.S):
+            ro.run(k)
+            for layer in range(w.n_layers):
+                check_publish(ro, k, layer)
+                worst = max(worst, check_attention(ro, k, layer))
+    finally:
+        ro.close()
+    _log(f"  max abs err {worst:.3e}, {ro.fp8_bound_ratio:.2f} x the bound at worst")
+
+
+@pytest.mark.timeout(600)
+def test_full_size_wan13b_4step_fp8k_sampled():
+    """The 1.3B 4-step round over 8-bit-key pages: steady state with the
+    anchor re-rotated (k=14), first and last layer, 64 sampled rows per
+    (group, head) plus the last row; whole pages."""
+    w = WAN13B_4STEP_FP8K
+    ro = Rollout(w)
+    try:
+        for k in range(15):
+            _log(f"{w.name} round {k}")
+            ro.run(k)
+            if k in (4, 14):
+                for layer in (0, w.n_layers - 1):
+                    check_publish(ro, k, layer)
+                    err = check_attention(ro, k, layer, rows=64)
+                    _log(f"  k={k} layer={layer} max abs err {err:.3e}, "
+                         f"{ro.fp8_bound_ratio:.2f} x the bound at worst")
     finally:
         ro.close()
