@@ -34,10 +34,12 @@
 //     while the other runs the softmax; the MFMA wave runs at raised issue
 //     priority (s_setprio).
 //   * Online softmax in base 2.  The Q fragments carry the scale and the QK
-//     accumulators start from minus the running max, so the product is
-//     already the exponent of P.  O and l are rescaled only when a row max
-//     grows by more than 2^8.  The row sum of P(t-1) is taken in the MFMA
-//     cluster of tile t, where the wave's VALU slots are otherwise idle.
+//     accumulators start from minus the running max (and a bias of 2^-7), so
+//     the product is already the exponent of P.  Whether a row max grew by
+//     2^8 or more is read off the rounded weights' exponent bits (one OR per
+//     tile, no row max); only then are the tile's scores recomputed and O, l
+//     rescaled.  The row sum of P(t-1) is taken in the MFMA cluster of tile
+//     t, where the wave's VALU slots are otherwise idle.
 //
 // fp32 instance (head_dim <= 128, % 4): a plain tiled kernel (4 lanes per
 // query, 32-key LDS tiles, fp32 FMA), used for fp32 rounds.
@@ -103,7 +105,6 @@ __global__ __launch_bounds__(512, 1) void wf_attention_bf16_kernel(const AttnArg
   constexpr int VROWS = NT / VCH;   // Vt rows covered by one load round
   constexpr int NPV = 4 * DT;       // PV MFMAs per tile
   constexpr int NQK = 2 * KSTEPS;   // QK MFMAs per tile
-  constexpr float kRescale = 8.f;   // lazy rescale threshold (log2 units)
   static_assert(KCH >= 8 && KLOADS * NT == BN * KCH && VLOADS * NT == D * VCH, "shape");
 
   __shared__ __attribute__((aligned(16))) __bf16 lds[STAGES][KTILE + VTILE];
@@ -230,8 +231,9 @@ __global__ __launch_bounds__(512, 1) void wf_attention_bf16_kernel(const AttnArg
   for (int i = 0; i < DT; ++i) oacc[i] = f32x16{};
   f32x16 sacc[2];
   bf16x8 pf[2][2];
-  // The QK accumulators start from moff = -m (m = this lane's running max),
-  // so they hold c s - m and P = exp2(S) needs no per-score arithmetic.
+  // The QK accumulators start from moff = -m - kBias (m = this lane's
+  // running max), so they hold c s - m - kBias and P' = exp2(S) needs no
+  // per-score arithmetic.
   f32x16 moff = f32x16{};
   bool first_tile = true;
   float l_run = 0.f;
@@ -291,7 +293,26 @@ __global__ __launch_bounds__(512, 1) void wf_attention_bf16_kernel(const AttnArg
   };
 
   // ---- VALU cluster: online softmax of S(t) (base 2, lazy rescale) ----
-  auto softmax = [&](int valid) {
+  // The accumulators hold S - m - kBias (m = the lane's running max), so the
+  // weights come out as P' = 2^(S - m - kBias); numerator and denominator
+  // share the factor 2^-kBias.  A weight reaches 2 (bf16 exponent field
+  // >= 128: bit 14 of its half-word) exactly when S - m >= kBias + 1 = 8, so
+  // one OR over the rounded weights tells whether m must move (lazy rescale
+  // at 2^8) without a row max.  Then -- rarely -- the tile's scores are
+  // multiplied again from LDS (the stage is intact until two clusters
+  // later), the row max is taken and O, l and the weights are redone with
+  // the new m.  The first tile takes the row max to start m.
+  constexpr float kBias = 7.f;
+  auto qk_again = [&](int qk_stage) {
+    const char* kbase = lds_bytes + qk_stage * kStageBytes;
+#pragma unroll
+    for (int j = 0; j < NQK; ++j) {
+      const int s = j >> 1, t2 = j & 1;
+      const bf16x8 f = *reinterpret_cast<const bf16x8*>(kbase + ka + (t2 * 32 * KPITCH + s * 16) * 2);
+      sacc[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qf[s], s == 0 ? moff : sacc[t2], 0, 0, 0);
+    }
+  };
+  auto mask = [&](int valid) {
     // value v of tile t2 is key 32 t2 + 16 (v / 8) + 8 half + (v % 8)
     if (valid < BN) {
 #pragma unroll
@@ -300,7 +321,10 @@ __global__ __launch_bounds__(512, 1) void wf_attention_bf16_kernel(const AttnArg
         for (int v = 0; v < 16; ++v)
           if (32 * t2 + 16 * (v >> 3) + 8 * half + (v & 7) >= valid) sacc[t2][v] = -__builtin_inff();
     }
-    // max of the lane's 32 values (c s - m) as a tree of 3-input maxima
+  };
+  // m += up with up = the row max's growth (first tile: the row max itself)
+  auto move_max = [&](bool first) {
+    // max of the lane's 32 values as a tree of 3-input maxima, both halves
     float r[11];
 #pragma unroll
     for (int i = 0; i < 10; ++i) {
@@ -310,30 +334,48 @@ __global__ __launch_bounds__(512, 1) void wf_attention_bf16_kernel(const AttnArg
     r[10] = fmaxf(sacc[1][14], sacc[1][15]);
     const float r0 = fmaxf(fmaxf(r[0], r[1]), r[2]), r1 = fmaxf(fmaxf(r[3], r[4]), r[5]);
     const float r2 = fmaxf(fmaxf(r[6], r[7]), r[8]), r3 = fmaxf(r[9], r[10]);
-    const float mx = pair_max32(fmaxf(fmaxf(r0, r1), fmaxf(r2, r3)));
-    // Lazy rescale: m moves only when some lane's max exceeds it by 2^8
-    // (always on the first tile).  Lanes whose max did not grow keep m.
-    if (first_tile || __any(mx > kRescale)) {
-      const float up = first_tile ? mx : fmaxf(mx, 0.f);
-      if (!first_tile) {
-        const float alpha = __builtin_amdgcn_exp2f(-up);
-        l_run *= alpha;
+    const float mx = pair_max32(fmaxf(fmaxf(r0, r1), fmaxf(r2, r3))) + kBias;
+    const float up = first ? mx : fmaxf(mx, 0.f);
+    if (!first) {
+      const float alpha = __builtin_amdgcn_exp2f(-up);
+      l_run *= alpha;
 #pragma unroll
-        for (int i = 0; i < DT; ++i) oacc[i] *= alpha;
-      }
-      first_tile = false;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        sacc[0][v] -= up;
-        sacc[1][v] -= up;
-        moff[v] -= up;
-      }
+      for (int i = 0; i < DT; ++i) oacc[i] *= alpha;
     }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      sacc[0][v] -= up;
+      sacc[1][v] -= up;
+      moff[v] -= up;
+    }
+  };
+  auto weights = [&]() {
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
       for (int v = 0; v < 16; ++v)
         pf[t2][v >> 3][v & 7] = static_cast<__bf16>(__builtin_amdgcn_exp2f(sacc[t2][v]));
+  };
+  auto softmax = [&](int valid, int qk_stage) {
+    mask(valid);
+    if (first_tile) {
+      first_tile = false;
+      move_max(true);
+    }
+    weights();
+    u32x4 w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = __builtin_bit_cast(u32x4, pf[i >> 1][i & 1]);
+    const uint32_t o0 = w[0][0] | w[0][1] | w[0][2], o1 = w[0][3] | w[1][0] | w[1][1];
+    const uint32_t o2 = w[1][2] | w[1][3] | w[2][0], o3 = w[2][1] | w[2][2] | w[2][3];
+    const uint32_t o4 = w[3][0] | w[3][1] | w[3][2];
+    const uint32_t any_big = (o0 | o1 | o2) | (o3 | o4 | w[3][3]);
+    if (__any((any_big & 0x40004000u) != 0u)) {
+      qk_again(qk_stage);
+      mask(valid);
+      move_max(false);
+      weights();
+    }
   };
 
   // ---- prologue: tiles 0..2 into stages 0..2.  The first MFMA cluster
@@ -384,7 +426,7 @@ __global__ __launch_bounds__(512, 1) void wf_attention_bf16_kernel(const AttnArg
         load_next();
         staged = true;
       }
-      softmax(t < n_full ? BN : tail);
+      softmax(t < n_full ? BN : tail, t & (STAGES - 1));
     }
     __syncthreads();
   }

@@ -27,11 +27,12 @@
 // Schedule as the bf16 instance: 8 waves x 32 queries in two ping-pong
 // groups of 4 (waves i and i+4 share a SIMD), one group in its MFMA cluster
 // (PV of tile t-1, QK of tile t, at raised issue priority) while the other
-// runs its softmax; a 4-stage LDS ring of K (XOR-swizzled 16-byte chunks)
-// and Vt (rows padded by one chunk) tiles, tile t+3 fetched into registers
-// while tile t is multiplied.  Online softmax in base 2; the QK accumulators
-// start from minus the running max; lazy rescale (2^8); the row sum of the
-// rounded weights is taken in the MFMA cluster.
+// runs its softmax; a 4-stage LDS ring of K and Vt tiles (rows padded by one
+// 16-byte chunk), tile t+3 fetched into registers while tile t is
+// multiplied.  Online softmax in base 2; the QK accumulators start from
+// minus the running max; lazy rescale (2^8) detected from the rounded
+// weights' exponent bits; the row sum of the rounded weights is taken in the
+// MFMA cluster.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -53,12 +54,13 @@ constexpr int kBN = 64;                   // keys per tile
 constexpr int kNT = 512;                  // threads: 8 waves in two groups of 4
 constexpr int kStages = 4;
 constexpr int kVPitch = kBN + 8;          // Vt row pitch in LDS (bf16 elements)
-constexpr int kKTile = kBN * kD;          // bytes of a K tile (64 rows x 128 codes)
+constexpr int kKPitch = kD + 16;          // K row pitch in LDS (bytes)
+constexpr int kKTile = kBN * kKPitch;     // bytes of a padded K tile
 constexpr int kVTile = kD * kVPitch * 2;  // bytes of a padded Vt tile
 constexpr int kStage = kKTile + kVTile;
 constexpr int kVLoads = kD * (kBN / 8) / kNT;   // 16-byte Vt chunks per thread
 constexpr int kE8M0One = 127;             // scale code of 2^0
-static_assert(kVLoads * kNT == kD * (kBN / 8) && kKTile == 16 * kNT, "shape");
+static_assert(kVLoads * kNT == kD * (kBN / 8) && kBN * kD == 16 * kNT, "shape");
 
 __device__ inline int find_group(const AttnArgs& a, int item) {
   int g = 0;
@@ -66,10 +68,10 @@ __device__ inline int find_group(const AttnArgs& a, int item) {
   return g;
 }
 
-// Byte offset of 16-byte chunk c of K row r inside a stage.  A QK operand
-// read by 16 lanes covers 16 consecutive keys at one chunk index; swizzling
-// the chunk by bits 1..3 of the row puts them in 16 different bank groups.
-__device__ inline int k_off(int r, int c) { return r * kD + ((c ^ ((r >> 1) & 7)) << 4); }
+// Byte offset of 16-byte chunk c of K row r inside a stage.  Rows are padded
+// by one chunk: a QK operand read by 16 lanes covers 16 consecutive keys at
+// one chunk index, 9 r + c mod 16 differs for all of them.
+__device__ inline int k_off(int r, int c) { return r * kKPitch + (c << 4); }
 
 // Key of A-operand row r of QK MFMA t2 (see the header).
 __device__ inline int qk_key(int t2, int r) {
@@ -101,7 +103,6 @@ __device__ inline uint32_t pack4(float a, float b, float c, float d) {
 
 __global__ __launch_bounds__(kNT, 1) void wf_attention_fp8k_kernel(const AttnArgs a) {
   constexpr int BM = kAttnBM_fp8k;
-  constexpr float kRescale = 8.f;         // lazy rescale threshold (log2 units)
   constexpr int NPV = 16;                 // PV MFMAs per tile (4 k-steps x 4 dim tiles)
   constexpr int NQK = 4;                  // QK MFMAs per tile (2 k-steps x 2 key halves)
   __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * kStage];
@@ -210,13 +211,8 @@ __global__ __launch_bounds__(kNT, 1) void wf_attention_fp8k_kernel(const AttnArg
   // LDS operand offsets of this lane: QK MFMA (t2, s) reads K row
   // qk_key(t2, col), chunks 4 s + 2 half + {0, 1}; PV MFMA (kk, dt) reads Vt
   // row 32 dt + col, keys 16 kk + 8 half ...
-  int ka[2][2][2];
-#pragma unroll
-  for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) ka[t2][s][u] = k_off(qk_key(t2, col), 4 * s + 2 * half + u);
+  // (qk_key(1, r) = qk_key(0, r) + 32: one base plus immediates)
+  const int ka = k_off(qk_key(0, col), 2 * half);
   const int va = kKTile + (col * kVPitch + 8 * half) * 2;
 
   f32x16 oacc[4];
@@ -224,8 +220,9 @@ __global__ __launch_bounds__(kNT, 1) void wf_attention_fp8k_kernel(const AttnArg
   for (int i = 0; i < 4; ++i) oacc[i] = f32x16{};
   f32x16 sacc[2];
   bf16x8 pf[2][2];
-  // The QK accumulators start from moff = -m (m = this lane's running max),
-  // so they hold S - m and P = exp2(S) needs no per-score arithmetic.
+  // The QK accumulators start from moff = -m - kBias (m = this lane's
+  // running max), so they hold S - m - kBias and P' = exp2(S) needs no
+  // per-score arithmetic.
   f32x16 moff = f32x16{};
   bool first_tile = true;
   float l_run = 0.f;
@@ -250,8 +247,8 @@ __global__ __launch_bounds__(kNT, 1) void wf_attention_fp8k_kernel(const AttnArg
         f.hi = f.lo;
       } else {
         const int j = i - NPV, s = j >> 1, t2 = j & 1;
-        f.lo = *reinterpret_cast<const u32x4*>(kb + ka[t2][s][0]);
-        f.hi = *reinterpret_cast<const u32x4*>(kb + ka[t2][s][1]);
+        f.lo = *reinterpret_cast<const u32x4*>(kb + ka + t2 * 32 * kKPitch + 64 * s);
+        f.hi = *reinterpret_cast<const u32x4*>(kb + ka + t2 * 32 * kKPitch + 64 * s + 16);
       }
       return f;
     };
@@ -302,7 +299,35 @@ __global__ __launch_bounds__(kNT, 1) void wf_attention_fp8k_kernel(const AttnArg
   };
 
   // ---- VALU cluster: online softmax of S(t) (base 2, lazy rescale) ----
-  auto softmax = [&](int valid) {
+  // The accumulators hold S - m - kBias (m = the lane's running max), so the
+  // weights come out as P' = 2^(S - m - kBias); numerator and denominator
+  // share the factor 2^-kBias.  A weight reaches 2 (bf16 exponent field
+  // >= 128: bit 14 of its half-word) exactly when S - m >= kBias + 1 = 8, so
+  // one OR over the rounded weights tells whether m must move (lazy rescale
+  // at 2^8) without a row max.  Then -- rarely -- the tile's scores are
+  // multiplied again from LDS (the stage is intact until two clusters
+  // later, and kcode still holds this tile's K scale), the row max is taken
+  // and O, l and the weights are redone with the new m.  The first tile
+  // takes the row max to start m.
+  constexpr float kBias = 7.f;
+  auto qk_again = [&](int qk_stage) {
+    const uint8_t* kb = lds + qk_stage * kStage;
+#pragma unroll
+    for (int j = 0; j < NQK; ++j) {
+      const int s = j >> 1, t2 = j & 1;
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(kb + ka + t2 * 32 * kKPitch + 64 * s);
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(kb + ka + t2 * 32 * kKPitch + 64 * s + 16);
+      i32x8 kf;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kf[e] = static_cast<int>(lo[e]);
+        kf[4 + e] = static_cast<int>(hi[e]);
+      }
+      sacc[t2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qf[s], s == 0 ? moff : sacc[t2], 0, 0, 0,
+                                                                 kcode, 0, qscale);
+    }
+  };
+  auto mask = [&](int valid) {
     // value v of sacc[t2] in lane half h is key 32 t2 + 16 (v / 8) + 8 h + (v % 8)
     if (valid < kBN) {
 #pragma unroll
@@ -311,7 +336,10 @@ __global__ __launch_bounds__(kNT, 1) void wf_attention_fp8k_kernel(const AttnArg
         for (int v = 0; v < 16; ++v)
           if (32 * t2 + 16 * (v >> 3) + 8 * half + (v & 7) >= valid) sacc[t2][v] = -__builtin_inff();
     }
-    // max of the lane's 32 values (S - m) as a tree of 3-input maxima
+  };
+  // m += up with up = the row max's growth (first tile: the row max itself)
+  auto move_max = [&](bool first) {
+    // max of the lane's 32 values as a tree of 3-input maxima, both halves
     float r[11];
 #pragma unroll
     for (int i = 0; i < 10; ++i) {
@@ -321,30 +349,48 @@ __global__ __launch_bounds__(kNT, 1) void wf_attention_fp8k_kernel(const AttnArg
     r[10] = fmaxf(sacc[1][14], sacc[1][15]);
     const float r0 = fmaxf(fmaxf(r[0], r[1]), r[2]), r1 = fmaxf(fmaxf(r[3], r[4]), r[5]);
     const float r2 = fmaxf(fmaxf(r[6], r[7]), r[8]), r3 = fmaxf(r[9], r[10]);
-    const float mx = pair_max32(fmaxf(fmaxf(r0, r1), fmaxf(r2, r3)));
-    // Lazy rescale: m moves only when some lane's max exceeds it by 2^8
-    // (always on the first tile).  Lanes whose max did not grow keep m.
-    if (first_tile || __any(mx > kRescale)) {
-      const float up = first_tile ? mx : fmaxf(mx, 0.f);
-      if (!first_tile) {
-        const float alpha = __builtin_amdgcn_exp2f(-up);
-        l_run *= alpha;
+    const float mx = pair_max32(fmaxf(fmaxf(r0, r1), fmaxf(r2, r3))) + kBias;
+    const float up = first ? mx : fmaxf(mx, 0.f);
+    if (!first) {
+      const float alpha = __builtin_amdgcn_exp2f(-up);
+      l_run *= alpha;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) oacc[i] *= alpha;
-      }
-      first_tile = false;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        sacc[0][v] -= up;
-        sacc[1][v] -= up;
-        moff[v] -= up;
-      }
+      for (int i = 0; i < 4; ++i) oacc[i] *= alpha;
     }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      sacc[0][v] -= up;
+      sacc[1][v] -= up;
+      moff[v] -= up;
+    }
+  };
+  auto weights = [&]() {
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
       for (int v = 0; v < 16; ++v)
         pf[t2][v >> 3][v & 7] = static_cast<__bf16>(__builtin_amdgcn_exp2f(sacc[t2][v]));
+  };
+  auto softmax = [&](int valid, int qk_stage) {
+    mask(valid);
+    if (first_tile) {
+      first_tile = false;
+      move_max(true);
+    }
+    weights();
+    u32x4 w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = __builtin_bit_cast(u32x4, pf[i >> 1][i & 1]);
+    const uint32_t o0 = w[0][0] | w[0][1] | w[0][2], o1 = w[0][3] | w[1][0] | w[1][1];
+    const uint32_t o2 = w[1][2] | w[1][3] | w[2][0], o3 = w[2][1] | w[2][2] | w[2][3];
+    const uint32_t o4 = w[3][0] | w[3][1] | w[3][2];
+    const uint32_t any_big = (o0 | o1 | o2) | (o3 | o4 | w[3][3]);
+    if (__any((any_big & 0x40004000u) != 0u)) {
+      qk_again(qk_stage);
+      mask(valid);
+      move_max(false);
+      weights();
+    }
   };
 
   // ---- prologue: tiles 0..2 into stages 0..2.  The first MFMA cluster
@@ -397,7 +443,7 @@ __global__ __launch_bounds__(kNT, 1) void wf_attention_fp8k_kernel(const AttnArg
         load_next();
         staged = true;
       }
-      softmax(ptp == T - 1 ? last_valid : kBN);
+      softmax(ptp == T - 1 ? last_valid : kBN, t & (kStages - 1));
       if (++ptp == T) ptp = 0;
       kcode = tcode[t + 1 < n_tiles ? t + 1 : t];
     }

@@ -21,7 +21,11 @@ from chunk_causal_dit_round_amd import wf
 from chunk_causal_dit_round_amd.workloads import (TINY_FP32, WAN13B_4STEP, WAN13B_4STEP_FP8,
                                                   WAN13B_4STEP_FP8K, WAN13B_5STEP, WAN13B_5STEP_ROLLING,
                                                   WAN14B_4STEP, Workload)
-from wfcheck import Rollout, check_attention, check_publish
+import numpy as np
+
+from oracle import wf_plan as P
+from oracle import wf_round as WR
+from wfcheck import Rollout, check_attention, check_publish, oracle_cfg
 
 pytestmark = pytest.mark.gpu
 
@@ -249,3 +253,70 @@ def test_full_size_wan13b_4step_fp8k_sampled():
                          f"{ro.fp8_bound_ratio:.2f} x the bound at worst")
     finally:
         ro.close()
+
+
+class GrowingKeys(Rollout):
+    """Keys of chunk i scaled by 1 + 0.8 i: along the context (anchor first,
+    then history oldest first) a query row's running max keeps growing by
+    several units of log2, so the kernels' lazy rescale fires after the
+    first tile, not only on it."""
+
+    def input_slice(self, rnd, layer, stage, name):
+        x = super().input_slice(rnd, layer, stage, name)
+        if name == "k":
+            x = (x.float() * (1.0 + 0.8 * (rnd - stage))).to(x.dtype)
+        return x
+
+
+def _rescale_events(ro, k, layer, fp8):
+    """(row, head, tile) triples of round k where the exact running row max
+    (base-2 units, tiles in the kernel's order) grows by at least 9 after
+    the first tile: the kernels must move m there (their trigger is 8)."""
+    w, oc = ro.w, oracle_cfg(ro.w)
+    c = WR.scale_of(oc) / np.log(2.0)
+    n = 0
+    for st in range(w.S + 1):
+        if not P.chunk_active(oc, k - st):
+            continue
+        kk, _ = WR.group_keys(oc, k, st, layer, ro.raw, fp8=fp8)
+        q = WR.q_rot(oc, k, st, layer, ro.raw)
+        n_keys = kk.shape[0]
+        if fp8:
+            # page-aligned 64-key tiles, the last of each page partial
+            bounds = [p * w.n_tokens + min(64 * t, w.n_tokens)
+                      for p in range(n_keys // w.n_tokens) for t in range((w.n_tokens + 63) // 64)]
+        else:
+            bounds = list(range(0, n_keys, 64))
+        bounds.append(n_keys)
+        for h in range(w.n_heads):
+            sc = c * (q[:, h, :] @ kk[:, h, :].T)
+            tile_max = np.stack([sc[:, a:b].max(axis=1) for a, b in zip(bounds[:-1], bounds[1:])], 1)
+            run = np.maximum.accumulate(tile_max, axis=1)
+            n += int((run[:, 1:] - run[:, :-1] >= 9.0).sum())
+    return n
+
+
+@pytest.mark.parametrize("dtype", [wf.WF_BF16, wf.WF_FP8K], ids=["bf16", "fp8k"])
+def test_lazy_rescale_after_first_tile(dtype):
+    """Queries whose running max grows along the context: every round and
+    layer against the oracle, and the rounds checked are ones where the
+    oracle's scores require the rescale to fire after the first tile.  The
+    scores reach about 40 log2 units, so bf16 is held to its derived
+    per-element bound (``wfcheck.bf16_attention_tolerance``), not the fixed
+    2e-2 bar."""
+    w = Workload(f"growing_keys_{dtype}", S=2, W=3, n_chunk=7, F=2, Hh=6, Ww=12, n_heads=2,
+                 head_dim=128, n_layers=1, dtype=dtype)
+    ro = GrowingKeys(w)
+    fp8 = "k" if dtype == wf.WF_FP8K else False
+    events = 0
+    try:
+        for k in range(w.n_chunk + w.S):
+            ro.run(k)
+            check_attention(ro, k, 0, derived=True)
+            events += _rescale_events(ro, k, 0, fp8)
+    finally:
+        ro.close()
+    ratio = getattr(ro, "bound_ratio", 0.0) or getattr(ro, "fp8_bound_ratio", 0.0)
+    _log(f"  {events} (row, head, tile) rescale events after the first tile; "
+         f"{ratio:.2f} x the bound at worst")
+    assert events > 100
