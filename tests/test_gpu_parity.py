@@ -296,7 +296,7 @@ def _rescale_events(ro, k, layer, fp8):
     return n
 
 
-@pytest.mark.parametrize("dtype", [wf.WF_BF16, wf.WF_FP8K], ids=["bf16", "fp8k"])
+@pytest.mark.parametrize("dtype", [wf.WF_BF16, wf.WF_FP8K, wf.WF_FP8], ids=["bf16", "fp8k", "fp8"])
 def test_lazy_rescale_after_first_tile(dtype):
     """Queries whose running max grows along the context: every round and
     layer against the oracle, and the rounds checked are ones where the
@@ -307,7 +307,7 @@ def test_lazy_rescale_after_first_tile(dtype):
     w = Workload(f"growing_keys_{dtype}", S=2, W=3, n_chunk=7, F=2, Hh=6, Ww=12, n_heads=2,
                  head_dim=128, n_layers=1, dtype=dtype)
     ro = GrowingKeys(w)
-    fp8 = "k" if dtype == wf.WF_FP8K else False
+    fp8 = {wf.WF_FP8K: "k", wf.WF_FP8: True}.get(dtype, False)
     events = 0
     try:
         for k in range(w.n_chunk + w.S):

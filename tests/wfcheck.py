@@ -25,7 +25,89 @@ BF16_RTOL = 2.0 ** -7
 ATT_TOL = {wf.WF_BF16: 2e-2, wf.WF_F32: 1e-4}
 
 
-def fp8_attention_tolerance(q8, k8, v8, scale, weight_eps=2.0 ** -4, out_rel=0.0):
+# The kernels rotate q and k in fp32 (fp32 tables); the oracle rotates in fp64.
+# Their difference is below ROT_ERR times the largest element of the row (q)
+# or of the page head (k); the page checks assert the same bound.
+ROT_ERR = 2.0 ** -21
+
+
+def _rotation_error(x):
+    """Per-element bound on |fp32 rotation - exact| for rotated rows x [.., d]
+    (pairs (2p, 2p+1) rotate together).  out = a cos - b sin with a, b exact
+    in fp32 and cos, sin rounded to fp32: each product and the difference
+    round once, so |err| <= 2^-23 (|a| + |b|) + 2^-24 |out| + O(2^-46), and
+    |a| + |b| <= sqrt(2) times the pair's norm, which the rotation keeps.
+    Doubled for margin."""
+    pair = np.hypot(x[..., 0::2], x[..., 1::2])
+    err = np.repeat(pair * (2.0 ** -22 * math.sqrt(2.0)), 2, axis=-1)
+    err += 2.0 ** -23 * np.abs(x)
+    return err
+
+
+def _midpoint_distance(y, mant_bits, min_exp):
+    """Distance from |y| to the nearest rounding midpoint of a floating-point
+    grid with ``mant_bits`` stored mantissa bits and smallest normal
+    exponent ``min_exp`` (0 exactly on a tie), and the grid spacing there
+    (the larger one next to |y|).  In the binade [2^E, 2^(E+1)) the grid
+    steps by u = 2^(E - mant_bits) and the midpoints sit at odd multiples of
+    u / 2; just above 2^E the nearest midpoint can be the one below 2^E, half
+    the lower binade's step away from 2^E.  Below 2^min_exp the step is that
+    of the lowest binade."""
+    a = np.abs(y)
+    _, ex = np.frexp(np.maximum(a, 2.0 ** min_exp))     # a in [2^(ex-1), 2^ex)
+    u = np.ldexp(1.0, ex - 1 - mant_bits)
+    f = a / u
+    f -= np.floor(f)
+    f -= 0.5
+    dist = np.abs(f)
+    dist *= u
+    below = a - np.ldexp(1.0, ex - 1)
+    below += u / 4                                       # midpoint under 2^E
+    np.minimum(dist, np.where(ex - 1 > min_exp, below, np.inf), out=dist)
+    return dist, u
+
+
+def key_flips(ke):
+    """Possible |k8 - k8_oracle| of one page head (``ke`` [N, d], the exact
+    rotated keys): one E4M3 step where the kernel's fp32 rotation may round
+    to the other side of a midpoint, 0 elsewhere.
+
+    A code is decided from the kernel's fp32 rotation; it can differ from the
+    oracle's (fp64 rotation) only where the exact value, scaled by its
+    64-token tile's power of two, lies within the rotation error of a
+    rounding midpoint (exactly on one only for pairs at angle 0, which both
+    sides rotate exactly)."""
+    n, d = ke.shape
+    n_t = -(-n // 64)
+    kp = np.zeros((n_t * 64, d))
+    kp[:n] = ke
+    amax = np.abs(kp.reshape(n_t, 64 * d)).max(axis=1)
+    # smallest e with amax <= 448 * 2^e (0 for an all-zero tile)
+    e = np.ceil(np.log2(np.maximum(amax, 1e-300) / 448.0))
+    e = np.where(amax > 448.0 * np.exp2(e), e + 1, e)
+    e = np.where(amax <= 448.0 * np.exp2(e - 1), e - 1, e)
+    e = np.where(amax == 0, 0.0, e)
+    sc = np.repeat(np.exp2(e), 64)[:, None]
+    dist, step = _midpoint_distance(kp / sc, 3, -6)
+    near = (dist > 0) & (dist * sc < _rotation_error(kp))
+    return np.where(near, step * sc, 0.0)[:n]
+
+
+def query_flips(q, q8, scale):
+    """Possible |q8 - q8_oracle| ([Nq, d]): the bf16 rounding of the exact
+    rotated query ``q`` can flip where it lies within the fp32 rotation
+    error of a bf16 midpoint, and then the row's E4M3 code of q times
+    scale * log2(e) may move one step."""
+    qdist, _ = _midpoint_distance(q, 7, -126)
+    qnear = (qdist > 0) & (qdist < _rotation_error(q))
+    c = scale * math.log2(math.e)
+    rows = np.abs(q8 * c).max(axis=1)
+    qsc = np.exp2(np.array([F8.pow2_exponent(r) for r in rows], dtype=np.float64))[:, None] / c
+    _, qstep = _midpoint_distance(q8 / qsc, 3, -6)
+    return np.where(qnear, qstep * qsc, 0.0)
+
+
+def fp8_attention_tolerance(q8, k8, v8, scale, weight_eps=2.0 ** -4, out_rel=0.0, flips=None):
     """Per-element bound on |O_gpu - O_oracle| over FP8 pages ([Nq, d] each).
 
     The oracle attends exactly over the dequantised Q, K and V.  The kernel
@@ -37,8 +119,16 @@ def fp8_attention_tolerance(q8, k8, v8, scale, weight_eps=2.0 ** -4, out_rel=0.0
     weight_eps / sqrt 3), six standard deviations of that sum (its
     denominator bounded below by (1 - weight_eps) sum_k P_k), plus out_rel
     |O| for the rounding of the output (bf16: 2^-8), plus 1e-3 for fp32
-    accumulation and the rare one-code differences between the kernel's fp32
-    and the oracle's fp64 rotation of Q and K.
+    accumulation.  ``flips`` = (dk, dq) from ``key_flips`` (per page, in
+    context order) and ``query_flips``: codes that the kernel's fp32
+    rotation may decide one step away from the oracle's.
+      * A key element off by dk_kd moves score k of row i by at most
+        f_ik = scale sum_d |q8_id| dk_kd, so weight k moves by at most a
+        factor exp(f_ik) and O by at most sum_k w_k |V_k - O| / (1 - sum_k w_k)
+        with w_k = P_k (exp(f_ik) - 1) (|V_k - O| <= |V_k| + |O|).
+      * A query element off by dq_id moves every score of row i by
+        scale dq_id k_kd, one sign for all keys: to first order O moves by
+        scale dq_id Cov_P(k_d, V), taken 1.25 times for the second order.
     """
     s = scale * (q8 @ k8.T)
     s -= s.max(axis=1, keepdims=True)
@@ -49,7 +139,18 @@ def fp8_attention_tolerance(q8, k8, v8, scale, weight_eps=2.0 ** -4, out_rel=0.0
     p2 = p * p
     var = p2 @ (v8 * v8) - 2.0 * o * (p2 @ v8) + o * o * p2.sum(axis=1, keepdims=True)
     spread = np.sqrt(np.maximum(var, 0.0)) / (ps * (1.0 - weight_eps))
-    return 6.0 * weight_eps / math.sqrt(3.0) * spread + out_rel * np.abs(o) + 1e-3
+    tol = 6.0 * weight_eps / math.sqrt(3.0) * spread + out_rel * np.abs(o) + 1e-3
+    if flips is not None:
+        dk, dq = flips
+        pn = p / ps
+        w = pn * np.expm1(scale * (np.abs(q8) @ dk.T))
+        ws = w.sum(axis=1, keepdims=True)
+        tol = tol + (w @ np.abs(v8) + ws * np.abs(o)) / np.maximum(1.0 - ws, 0.5)
+        for i in np.nonzero(dq.any(axis=1))[0]:
+            pk = k8 * pn[i][:, None]
+            cov = pk.T @ v8 - np.outer(pk.sum(axis=0), o[i])      # Cov_P(k_d, V_e)
+            tol[i] += 1.25 * scale * (dq[i] @ np.abs(cov))
+    return tol
 
 
 def bf16_attention_tolerance(q, k, v, scale):
@@ -285,6 +386,17 @@ def check_attention(ro, k, layer, rows=None, heads=None, stages=None, seed=0, de
     tol = ATT_TOL.get(w.dtype)
     worst = 0.0
     rng = np.random.default_rng([seed, k, layer])
+    flips_of = {}
+
+    def page_flips(kind, chunk, hs):
+        """key_flips of one context page (all selected heads), once per call."""
+        if (kind, chunk) not in flips_of:
+            rnd, cell, frame0 = WR.entry_source(oc, k, kind, chunk)
+            kr = rope3d(np.asarray(ro.raw(rnd, layer, cell, "k"), dtype=np.float64)[:, hs, :],
+                        frame0, w.F, w.Hh, w.Ww, oc.rope_theta)
+            flips_of[(kind, chunk)] = np.stack([key_flips(kr[:, i, :]) for i in range(len(hs))], 1)
+        return flips_of[(kind, chunk)]
+
     for st in (range(w.S + 1) if stages is None else stages):
         if not P.chunk_active(oc, k - st):
             continue
@@ -323,14 +435,18 @@ def check_attention(ro, k, layer, rows=None, heads=None, stages=None, seed=0, de
             if r is not None:
                 qr = qr[r]
             kk, vv = WR.group_keys(oc, k, st, layer, ro.raw, hs, fp8=fp8)
-            # weights rounded to E4M3 (FP8) or bf16 (FP8K, whose output
-            # rounding is then no longer inside the 1e-3 floor's margin)
-            eps, out_rel = (2.0 ** -4, 0.0) if fp8 is True else (2.0 ** -8, 2.0 ** -8)
+            dk = np.concatenate([page_flips(kind, chunk, hs)
+                                 for kind, chunk, _slot in P.key_entries(oc, k, st)], axis=0)
+            # weights rounded to E4M3 (FP8) or bf16 (FP8K); the output is
+            # bf16 on both (peaky rows have |O| near 1, where its rounding
+            # exceeds the 1e-3 floor)
+            eps, out_rel = (2.0 ** -4 if fp8 is True else 2.0 ** -8), 2.0 ** -8
             tol = np.empty_like(err)
             for hi, h in enumerate(hs):
                 q8 = F8.fp8_query(F8.bf16_round(qr[:, h, :]), WR.scale_of(oc))
+                flips = (dk[:, hi, :], query_flips(qr[:, h, :], q8, WR.scale_of(oc)))
                 tol[:, hi, :] = fp8_attention_tolerance(q8, kk[:, hi, :], vv[:, hi, :],
-                                                        WR.scale_of(oc), eps, out_rel)
+                                                        WR.scale_of(oc), eps, out_rel, flips)
             ratio = (err / tol).max()
             worst = max(worst, err.max())
             ro.fp8_bound_ratio = max(getattr(ro, "fp8_bound_ratio", 0.0), ratio)
