@@ -118,12 +118,15 @@ class DitRounds:
     reads the output of layer l-1 of the same cell in the same round; the
     attention of a layer reads the K/V that the producer steps of the same
     layer made for the chunks of its key list (``wf_round``), in whatever
-    round they were made.  Everything is memoised.
+    round they were made.  Everything is memoised.  ``fp8`` selects the page
+    reading of the attention (``wf_round.group_output``: FP8 pages, or "k"
+    for the 8-bit QK^T tier's FP8 keys with exact values).
     """
 
     def __init__(self, cfg: P.Config, x0: Callable, weights: Callable, mod: Callable,
-                 eps: float = EPS):
+                 eps: float = EPS, fp8=False):
         self.cfg, self.x0, self.weights, self.mod, self.eps = cfg, x0, weights, mod, eps
+        self.fp8 = fp8          # the page reading of the attention (``wf_round``)
         self._x: Dict = {}
         self._qkv: Dict = {}
 
@@ -150,7 +153,7 @@ class DitRounds:
         return self.qkv(rnd, layer, stage)["qkv".index(name)]
 
     def attention(self, rnd: int, layer: int, stage: int, rows=None) -> np.ndarray:
-        return R.group_output(self.cfg, rnd, stage, layer, self.raw, rows=rows)
+        return R.group_output(self.cfg, rnd, stage, layer, self.raw, rows=rows, fp8=self.fp8)
 
     def layer_output(self, rnd: int, layer: int, stage: int,
                      rows: Optional[np.ndarray] = None) -> np.ndarray:

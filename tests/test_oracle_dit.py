@@ -10,6 +10,8 @@ Pinned against something other than the oracle itself:
   row whatever the keys and positions are;
 * the causal invariant through two layers: a noisier cell's input never
   reaches a cleaner cell's output.
+The last two also over FP8 pages and the 8-bit QK^T tier's pages (the
+attention's page reading is pinned in ``test_oracle_fp8.py``).
 """
 
 import math
@@ -122,7 +124,7 @@ def _tiny_cfg(n_layers=1):
                     n_heads=2, head_dim=16, n_layers=n_layers, mask=0)
 
 
-def _rounds(cfg, seed, mod_fn=None, x_fn=None):
+def _rounds(cfg, seed, mod_fn=None, x_fn=None, fp8=False):
     r = _rng(seed)
     C, F = cfg.n_heads * cfg.head_dim, 64
     ws = [_weights(r, C, F) for _ in range(cfg.n_layers)]
@@ -138,7 +140,7 @@ def _rounds(cfg, seed, mod_fn=None, x_fn=None):
                 cache[(rnd, stage)] = x_fn(rnd, stage, cache[(rnd, stage)])
         return cache[(rnd, stage)]
 
-    return D.DitRounds(cfg, x0, lambda l: ws[l], lambda l: mods[l]), ws, mods
+    return D.DitRounds(cfg, x0, lambda l: ws[l], lambda l: mods[l], fp8=fp8), ws, mods
 
 
 def test_zero_gates_give_identity():
@@ -155,10 +157,15 @@ def test_zero_gates_give_identity():
         assert np.array_equal(dr.layer_output(5, 0, s), dr.x_in(5, 0, s))
 
 
-def test_constant_values_pass_through_attention():
+@pytest.mark.parametrize("fp8", [False, "k", True], ids=["exact", "fp8_keys", "fp8_pages"])
+def test_constant_values_pass_through_attention(fp8):
     """scale1 = -1 and one shift1 for every stage: a = shift1 for every token
     of every cell, so every value row is shift1 W_v^T + b_v and attention
-    returns it whatever RoPE, paging and the softmax do."""
+    returns it whatever RoPE, paging, the key quantisation and the softmax
+    do.  Over FP8 pages the values are quantised too: each head's row then
+    comes back as its E4M3 quantisation with the row's own power-of-two
+    scale (every 64-token tile holds the same rows)."""
+    from oracle import wf_fp8 as F8
     cfg = _tiny_cfg()
     r = _rng(5)
     shift = r.standard_normal(cfg.n_heads * cfg.head_dim)
@@ -169,10 +176,14 @@ def test_constant_values_pass_through_attention():
         m[:, 0] = shift
         return m
 
-    dr, ws, mods = _rounds(cfg, 6, fix)
+    dr, ws, mods = _rounds(cfg, 6, fix, fp8=fp8)
     C = cfg.n_heads * cfg.head_dim
     w = ws[0]
     vrow = shift @ w.w_qkv[2 * C:].T + w.b_qkv[2 * C:]
+    if fp8 is True:
+        d = cfg.head_dim
+        vrow = np.concatenate([np.ldexp(F8.e4m3_values(c), e) for c, e in
+                               (F8.quantize_block(vrow[h * d:(h + 1) * d]) for h in range(cfg.n_heads))])
     k = 5                                     # full width, history and anchor present
     for s in range(cfg.S + 1):
         o = dr.attention(k, 0, s)
@@ -182,14 +193,15 @@ def test_constant_values_pass_through_attention():
         assert np.allclose(dr.layer_output(k, 0, s), expect, atol=1e-12)
 
 
-def test_causal_invariant_through_two_layers():
+@pytest.mark.parametrize("fp8", [False, "k"], ids=["exact", "fp8_keys"])
+def test_causal_invariant_through_two_layers(fp8):
     """Perturbing the input of a noisier cell (stage j < s) changes nothing
     at stage s, in either layer (WF §3.1, Eq. 4 mask 1[j >= s])."""
     cfg = _tiny_cfg(n_layers=2)
     k = 4
-    base, _, _ = _rounds(cfg, 7)
+    base, _, _ = _rounds(cfg, 7, fp8=fp8)
     bump = lambda rnd, stage, x: x + (5.0 if (rnd == k and stage == 0) else 0.0)  # noqa: E731
-    pert, _, _ = _rounds(cfg, 7, x_fn=bump)
+    pert, _, _ = _rounds(cfg, 7, x_fn=bump, fp8=fp8)
     for s in range(1, cfg.S + 1):
         assert np.array_equal(base.layer_output(k, 1, s), pert.layer_output(k, 1, s))
     assert not np.allclose(base.layer_output(k, 1, 0), pert.layer_output(k, 1, 0))
