@@ -30,7 +30,9 @@ Other modes (one JSON line each):
                      Wan-shaped block (norms, QKV / output / FFN products, qk norm,
                      publish, attention) for all S+1 cells, dummy weights, FFN
                      width --ffn (8960 for the 1.3B shape); whole-round TFLOP/s
-                     against the bf16 MFMA peak.  With --rollout: the whole
+                     against the bf16 MFMA peak (with --workload
+                     wan1.3b_4step_fp8k or _fp8: attention over those pages, the
+                     peak blended by FLOPs).  With --rollout: the whole
                      133-chunk request through the DiT.
 """
 
@@ -208,7 +210,8 @@ def dit_oracle_baseline(ds, w, k):
     mod = ds.mod[0].double().cpu().numpy()
     # round r starts from input set r % 2 on the GPU side
     x0 = lambda rnd, st: synth.dit_x0(ds.tag, rnd % 2, st, w.n_tokens, ds.C, ds.s.device).double().cpu().numpy()  # noqa: E731
-    dr = D.DitRounds(oc, x0, lambda l: wt, lambda l: mod)
+    fp8 = {2: True, 3: "k"}.get(w.dtype, False)          # FP8 / FP8K page readings
+    dr = D.DitRounds(oc, x0, lambda l: wt, lambda l: mod, fp8=fp8)
     rows = np.arange(0, w.n_tokens, w.n_tokens // 256)[:256]
     # projections of every page a steady round reads (one per cell and history page)
     t0 = time.perf_counter()
@@ -283,7 +286,7 @@ def dit_bench(args, w):
     """Steady whole-DiT rounds: wf_dit_round over all layers."""
     import torch
 
-    from chunk_causal_dit_round_amd import synth
+    from chunk_causal_dit_round_amd import synth, wf
     from chunk_causal_dit_round_amd.dit import DitSession
     from chunk_causal_dit_round_amd.session import Session
 
@@ -324,19 +327,25 @@ def dit_bench(args, w):
     attn_flops = plans[0].flops
     total = (gemm_flops + attn_flops) * args.steps
     achieved = total / elapsed / 1e12
+    # products at the bf16 peak, attention at its page type's peak: a round
+    # at both peaks takes gemm / 2.5 + attention / P_attn
+    kind = PAGE_KINDS[{wf.WF_FP8: "fp8", wf.WF_FP8K: "fp8k"}.get(w.dtype, "bf16")]
+    peak = (gemm_flops + attn_flops) / (gemm_flops / PEAK_BF16_TFLOPS + attn_flops / kind["peak"])
     res = {
         "mode": "dit",
         "metric": "DiT rounds/sec (=chunks/sec): whole Wan-shaped DiT forward of a wavefront round",
         "value": args.steps / elapsed, "unit": "rounds/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": 1e3 * elapsed / args.steps, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if kind["dtype"] == "bf16" else "bf16 products, attention " + kind["dtype"],
+        "data": "synthetic",
         "config": {"workload": f"{w.name} steady round, whole DiT forward (dummy weights)",
                    "S": S, "W": w.W, "W_store": w_store, "tokens_per_chunk": N, "heads": w.n_heads,
                    "head_dim": w.head_dim, "dim": C, "ffn_dim": ffn, "layers": L,
                    "rounds_timed": [k0, k0 + args.steps - 1]},
         "flops_per_round": {"products": gemm_flops, "attention": attn_flops},
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak,
+                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
                      "kernel": "whole round (products + attention)"},
     }
     if not args.no_cpu_baseline:

@@ -184,7 +184,9 @@ wf_status check_call(wf_handle* h, const wf_dit_config* dc, const wf_dit_weights
   wf_status s = check_dc(h, dc);
   if (s != WF_OK) return s;
   if (!h->bound) return fail(WF_EINVAL, "handle is not bound (call wf_bind first)");
-  if (h->sh.dtype != WF_BF16) return fail(WF_EUNSUPPORTED, "the DiT block runs bf16 rounds only");
+  // bf16 activations and weights; the pages may be bf16, FP8 or FP8 keys
+  // with bf16 values (their q/k/v/q_rot/out tensors are bf16 in all three)
+  if (h->sh.dtype == WF_F32) return fail(WF_EUNSUPPORTED, "the DiT block runs bf16 activations, not fp32 rounds");
   if (!w || !mod || !x || !work) return fail(WF_EINVAL, "weights, mod, x or work is NULL");
   if (!aligned16(mod) || !aligned16(x) || !aligned16(work))
     return fail(WF_EINVAL, "mod, x and work must be 16-byte aligned");

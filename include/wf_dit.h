@@ -34,12 +34,17 @@
  *   work    caller-owned device scratch of wf_dit_workspace_bytes() bytes
  *           (activations of one layer plus the GEMM library's workspace)
  *
+ * Pages: any page type of a bf16-activation round -- WF_BF16, WF_FP8 (FP8
+ * keys and values, App. C.6) or WF_FP8K (FP8 keys, bf16 values: the 8-bit
+ * Q K^T tier, App. B.1 / App. C.2 Tab. 4, whose "Sage" configuration keeps
+ * the linear layers in bf16 as this block does).  The attention then runs
+ * that page type's kernel; everything else is unchanged.
+ *
  * Ownership and errors follow wf.h.  One difference: the first call on a
  * handle creates a hipBLASLt handle (its own small host and device state,
  * freed by wf_destroy); the products run through hipBLASLt, every other step
- * through this library's kernels.  Only bf16 rounds have this block
- * (WF_EUNSUPPORTED for fp32 and FP8 pages); C must be a multiple of 8 and at
- * most 8192.
+ * through this library's kernels.  fp32 rounds have no block
+ * (WF_EUNSUPPORTED); C must be a multiple of 8 and at most 8192.
  */
 #ifndef WF_DIT_H
 #define WF_DIT_H

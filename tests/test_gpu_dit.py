@@ -1,5 +1,6 @@
 """GPU parity of the DiT block around the round (``include/wf_dit.h``)
-against the fp64 oracle (``oracle/wf_dit.py``), through the C ABI.
+against the fp64 oracle (``oracle/wf_dit.py``), through the C ABI, over
+bf16 pages and (with derived wider bounds) over FP8 and 8-bit-key pages.
 
 Small shapes: every round of a request, every active cell, every element of
 the residual stream after the last layer (two layers, so layer 1 reads
@@ -41,6 +42,29 @@ pytestmark = pytest.mark.gpu
 N_ROUNDINGS = 10
 SIGMA_BF16 = 2.0 ** -8 * (1.0 / (8.0 * math.log(2.0))) ** 0.5   # one RNE rounding, relative
 REL_TOL = 6 * SIGMA_BF16 * N_ROUNDINGS ** 0.5                  # 3.15e-2
+
+# Over FP8 pages the oracle quantises the exact q, k (and v) while the GPU
+# quantises its own, already rounded ones.  A perturbation delta of a value
+# flips its E4M3 code by one step u with probability 2 |delta| / u (the
+# value's distance to the nearer midpoint is uniform in [0, u/2]), so the
+# code's error has variance E[2 |delta| u] = 2 sqrt(2/pi) sigma_delta E[u]
+# for Gaussian delta; relative to the value, u = 2^-3 / m and, m
+# log-uniform, E[u] = 2^-3 / (2 ln 2).  The perturbations come from the
+# roundings upstream: k after a, qkv and its norm (3), q after those and
+# q_rot (4), v after a and qkv (2).  Each flipped operand then reaches the
+# update with gain about one, like the roundings above.  On FP8 pages the
+# softmax weights are rounded to E4M3 instead of bf16: standard deviation
+# 2^-4 sqrt(1 / (8 ln 2)) in place of one of the ten bf16 roundings.
+_EU = 2.0 ** -3 / (2.0 * math.log(2.0))
+
+
+def _flip_var(n_upstream):
+    return 2.0 * math.sqrt(2.0 / math.pi) * math.sqrt(n_upstream) * SIGMA_BF16 * _EU
+
+
+REL_TOL_FP8K = 6 * math.sqrt(N_ROUNDINGS * SIGMA_BF16 ** 2 + _flip_var(3) + _flip_var(4))
+REL_TOL_FP8 = 6 * math.sqrt((N_ROUNDINGS - 1) * SIGMA_BF16 ** 2 + (16 * SIGMA_BF16) ** 2
+                            + _flip_var(3) + _flip_var(4) + _flip_var(2))
 ABS_FLOOR = 1e-5
 
 
@@ -58,18 +82,19 @@ def _log(msg):
 
 def _oracle_rounds(ds: DitSession, w: Workload):
     cfg = oracle_cfg(w)
+    fp8 = {wf.WF_FP8: True, wf.WF_FP8K: "k"}.get(w.dtype, False)
     weights = [D.Weights(**{n: t.detach().double().cpu().numpy() for n, t in lw.items()})
                for lw in ds.layers]
     mods = [m.double().cpu().numpy() for m in ds.mod]
     x0 = lambda rnd, st: synth.dit_x0(ds.tag, rnd, st, w.n_tokens, ds.C, ds.s.device).double().cpu().numpy()  # noqa: E731
-    return D.DitRounds(cfg, x0, lambda l: weights[l], lambda l: mods[l])
+    return D.DitRounds(cfg, x0, lambda l: weights[l], lambda l: mods[l], fp8=fp8)
 
 
-def _compare(got, want, x_in, what):
+def _compare(got, want, x_in, what, rel_tol=REL_TOL):
     """Max error / bound over the rows; asserts the bound."""
     d = want - x_in
     rms = np.sqrt((d * d).mean(axis=1, keepdims=True))
-    bound = REL_TOL * rms + ABS_FLOOR
+    bound = rel_tol * rms + ABS_FLOOR
     err = np.abs(got - want)
     ratio = float((err / bound).max())
     assert ratio <= 1.0, f"{what}: max err/bound {ratio:.3f}, max err {err.max():.3g}"
@@ -164,6 +189,69 @@ def test_full_size_wan13b_one_layer_sampled():
             want = orc.layer_output(last, 0, st, rows=rows)
             x_in = orc.x_in(last, 0, st)[rows]
             worst = max(worst, _compare(got[st][rows], want, x_in, f"stage {st}"))
+        _log(f"{w.name}: worst err/bound {worst:.3f}")
+    finally:
+        s.close()
+
+
+FP8_SMALL = [
+    (SMALL[1][0].with_(name="dit_fp8k_s4_n360", dtype=wf.WF_FP8K), 512, REL_TOL_FP8K),
+    (SMALL[1][0].with_(name="dit_fp8_s4_n360", dtype=wf.WF_FP8), 512, REL_TOL_FP8),
+]
+
+
+@pytest.mark.parametrize("w,ffn,rel_tol", FP8_SMALL, ids=[w.name for w, _, _ in FP8_SMALL])
+def test_small_dit_over_fp8_pages_every_round(w, ffn, rel_tol):
+    """The block over 8-bit-key pages (the paper's Sage tier keeps the linear
+    layers in bf16) and over FP8 pages: every round, every element of x
+    after two layers, against the oracle's block over the same page reading.
+    Bound: the derivation above (3.15e-2 for bf16 pages becomes
+    REL_TOL_FP8K / REL_TOL_FP8 times rms_row(d))."""
+    s = Session(w.config(), io=False)
+    ds = DitSession(s, ffn, tag=w.name)
+    orc = _oracle_rounds(ds, w)
+    worst = 0.0
+    try:
+        for k in range(w.n_chunk + w.S):
+            plan = s.plan(k)
+            ds.load_x0(k)
+            ds.round(plan)
+            torch.cuda.synchronize()
+            got = ds.x.double().cpu().numpy()
+            for st in range(w.S + 1):
+                if not plan.cells[st].active:
+                    continue
+                want = orc.layer_output(k, w.n_layers - 1, st)
+                x_in = orc.x_in(k, 0, st)
+                worst = max(worst, _compare(got[st], want, x_in, f"{w.name} k={k} stage={st}", rel_tol))
+        _log(f"{w.name}: worst err/bound {worst:.3f} (bound {rel_tol:.3g} rms_row(d))")
+    finally:
+        s.close()
+
+
+def test_full_size_wan13b_one_layer_fp8k_sampled():
+    """1.3B shape, one layer, over 8-bit-key pages: rounds 0..S+1, 48
+    sampled rows per active cell of the last round against the oracle."""
+    w = WAN13B_4STEP.with_(name="dit_wan1.3b_l1_fp8k", n_layers=1, dtype=wf.WF_FP8K)
+    s = Session(w.config(), io=False)
+    ds = DitSession(s, 8960, tag=w.name)
+    orc = _oracle_rounds(ds, w)
+    last = w.S + 1
+    try:
+        for k in range(last + 1):
+            plan = s.plan(k)
+            ds.load_x0(k)
+            ds.round(plan)
+        torch.cuda.synchronize()
+        got = ds.x.double().cpu().numpy()
+        rng = np.random.default_rng(14)
+        worst = 0.0
+        for st in range(w.S + 1):
+            rows = np.sort(rng.choice(w.n_tokens, 48, replace=False))
+            rows[-1] = w.n_tokens - 1
+            want = orc.layer_output(last, 0, st, rows=rows)
+            x_in = orc.x_in(last, 0, st)[rows]
+            worst = max(worst, _compare(got[st][rows], want, x_in, f"stage {st}", REL_TOL_FP8K))
         _log(f"{w.name}: worst err/bound {worst:.3f}")
     finally:
         s.close()
