@@ -431,6 +431,7 @@ def main():
     elapsed = t1 - t0
     ms_step = 1e3 * elapsed / args.steps
     att_ms = [e[1][l].elapsed_time(e[2][l]) for e in events for l in range(L)]
+    round_ms = [e[0][0].elapsed_time(e[2][L - 1]) for e in events]     # device time per round
     pub_ms = [e[0][l].elapsed_time(e[1][l]) for e in events for l in range(L)]
     att_avg = sum(att_ms) / len(att_ms)
     pub_avg = sum(pub_ms) / len(pub_ms)
@@ -466,6 +467,9 @@ def main():
                      "kernel": kind["kernel"],
                      "flops_per_launch": flops_launch, "avg_launch_ms": att_avg},
         "attention_tflops_round": total_flops / elapsed / 1e12,
+        # one exp per readable (query, key, head): N_q N_k H = FLOPs / (4 d)
+        "softmax_exps_per_round": plans[0].flops / (4.0 * w.head_dim),
+        "median_round_ms": statistics.median(round_ms) if round_ms else None,
         "publish": {"avg_launch_ms": pub_avg, "bytes_per_launch": pub_bytes_launch,
                     "gbps": pub_bytes_launch / (pub_avg * 1e-3) / 1e9,
                     "hbm_frac": pub_bytes_launch / (pub_avg * 1e-3) / 1e9 / PEAK_HBM_GBPS},
