@@ -35,12 +35,6 @@ struct Shape {
   int Npad, T;
 };
 
-// FP8 / FP8K page sections (byte offsets inside a page).
-inline size_t fp8_v_offset(const Shape& sh) { return size_t(sh.H) * sh.Npad * sh.D; }
-inline size_t fp8_code_offset(const Shape& sh) {
-  return size_t(sh.dtype == WF_FP8K ? 3 : 2) * sh.H * sh.Npad * sh.D;
-}
-
 // Validates cfg (method-level rules only) and fills `out`.  Returns false
 // with a reason in `why` when the config is invalid.
 bool derive_shape(const wf_config* cfg, Shape* out, std::string* why);
