@@ -212,8 +212,8 @@ wf_status wf_pool_bytes(const wf_config* cfg, size_t* pool_bytes,
  * on the host in fp64, stored as fp32) with a synchronous copy.  Sizes are
  * checked first (WF_ESMALL), then kernel support for the config
  * (WF_EUNSUPPORTED: bf16 needs head_dim 64 or 128, N % 8 == 0, N >= 64 and
- * one layer's slots below 4 GiB; FP8 needs head_dim 128, N % 8 == 0, one
- * layer's slots below 4 GiB and (1 + max(W, W_store) + 1 + S) * T <= 4096;
+ * one layer's slots below 4 GiB; FP8 and FP8K need head_dim 128, N % 8 == 0,
+ * one layer's slots below 4 GiB and (1 + max(W, W_store) + 1 + S) * T <= 4096;
  * fp32 needs head_dim % 4 == 0, head_dim <= 128 and N % 4 == 0).  Buffers
  * must be 16-byte aligned.  The handle keeps the pointers, not the memory. */
 wf_status wf_bind(wf_handle* h, void* d_pool, size_t pool_bytes,
