@@ -25,8 +25,9 @@
 // work-group barrier per 64-key tile: an MFMA cluster (PV of tile t-1, row
 // sums, QK of tile t; 9 FP8 MFMAs) then the softmax of tile t and the
 // staging of tile t+2.  With the MFMA cluster this short, letting the two
-// waves of a SIMD drift between clusters measured faster than the bf16
-// instance's ping-pong between wave groups.  K and Vt tiles live in a
+// waves of a SIMD drift between clusters measured as fast as the bf16
+// instance's ping-pong between wave groups, with one barrier per tile
+// instead of two.  K and Vt tiles live in a
 // 4-stage LDS ring with 16-byte chunks XOR-swizzled per row (conflict-free
 // operand reads and stores).  Softmax in base 2 with lazy rescale; the QK
 // accumulators start from 2^7 divided by the running max (in exponent
