@@ -59,23 +59,34 @@ def _fp8_page(x: np.ndarray) -> np.ndarray:
     return out
 
 
-def group_keys(cfg: P.Config, k: int, stage: int, layer: int, raw, heads=None, fp8=False):
+def group_keys(cfg: P.Config, k: int, stage: int, layer: int, raw, heads=None, fp8=False,
+               pages=None):
     """Concatenated rotated keys and values of query stage ``stage``:
     ([N_k, H', d], [N_k, H', d]) in plan order (WF §3.1, Eq. 5).  With
     ``fp8`` each page is the FP8 page of the App. C.6 reading; with
-    ``fp8="k"`` only the keys are (8-bit QK^T tier, values exact)."""
+    ``fp8="k"`` only the keys are (8-bit QK^T tier, values exact).
+
+    ``pages``: an optional dict that keeps each page once it is made, for
+    callers that ask for several stages of the same round, layer, heads and
+    page reading (the stages share most of their pages)."""
     ks, vs = [], []
     for kind, chunk, _slot in P.key_entries(cfg, k, stage):
-        rnd, cell, frame0 = entry_source(cfg, k, kind, chunk)
-        kr = np.asarray(raw(rnd, layer, cell, "k"), dtype=np.float64)
-        vr = np.asarray(raw(rnd, layer, cell, "v"), dtype=np.float64)
-        if heads is not None:
-            kr, vr = kr[:, heads, :], vr[:, heads, :]
-        kr = rope3d(kr, frame0, cfg.F, cfg.Hh, cfg.Ww, cfg.rope_theta)
-        if fp8:
-            kr = _fp8_page(kr)
-            if fp8 != "k":
-                vr = _fp8_page(vr)
+        key = (kind, chunk)
+        if pages is not None and key in pages:
+            kr, vr = pages[key]
+        else:
+            rnd, cell, frame0 = entry_source(cfg, k, kind, chunk)
+            kr = np.asarray(raw(rnd, layer, cell, "k"), dtype=np.float64)
+            vr = np.asarray(raw(rnd, layer, cell, "v"), dtype=np.float64)
+            if heads is not None:
+                kr, vr = kr[:, heads, :], vr[:, heads, :]
+            kr = rope3d(kr, frame0, cfg.F, cfg.Hh, cfg.Ww, cfg.rope_theta)
+            if fp8:
+                kr = _fp8_page(kr)
+                if fp8 != "k":
+                    vr = _fp8_page(vr)
+            if pages is not None:
+                pages[key] = (kr, vr)
         ks.append(kr)
         vs.append(vr)
     return np.concatenate(ks, axis=0), np.concatenate(vs, axis=0)
@@ -88,20 +99,20 @@ def q_rot(cfg: P.Config, k: int, stage: int, layer: int, raw) -> np.ndarray:
 
 
 def group_output(cfg: P.Config, k: int, stage: int, layer: int, raw,
-                 rows=None, heads=None, fp8=False) -> np.ndarray:
+                 rows=None, heads=None, fp8=False, pages=None) -> np.ndarray:
     """Attention output of query stage ``stage``: [len(rows), len(heads), d].
 
     ``rows`` / ``heads`` select query tokens and heads (all by default);
     every selected row still attends to its full key list.  With ``fp8`` the
     pages are FP8 pages (``fp8="k"``: FP8 keys, exact values) and each
     rotated query row, stored in bf16, is scaled and quantised per row (App.
-    C.6 reading, ``wf_fp8.fp8_query``).
+    C.6 reading, ``wf_fp8.fp8_query``).  ``pages`` as in ``group_keys``.
     """
     heads = list(range(cfg.n_heads)) if heads is None else list(heads)
     qr = q_rot(cfg, k, stage, layer, raw)
     if rows is not None:
         qr = qr[np.asarray(rows)]
-    kk, vv = group_keys(cfg, k, stage, layer, raw, heads, fp8=fp8)
+    kk, vv = group_keys(cfg, k, stage, layer, raw, heads, fp8=fp8, pages=pages)
     out = np.empty((qr.shape[0], len(heads), cfg.head_dim), dtype=np.float64)
     sc = scale_of(cfg)
     for hi, h in enumerate(heads):

@@ -236,3 +236,29 @@ def test_fp8_keys_only_round_is_dense_attention_with_exact_values():
     assert np.array_equal(vv_k, vv)
     _, vv_kv = R.group_keys(cfg, k, stage, 0, raw, [0], fp8=True)
     assert not np.array_equal(vv_kv, vv)
+
+
+@pytest.mark.parametrize("fp8", [False, "k", True])
+def test_page_memo_changes_nothing(fp8):
+    """group_output with a shared page dict over every stage of a round gives
+    the same bits as building each stage's pages afresh."""
+    from oracle import wf_plan as P
+    from oracle import wf_round as R
+
+    cfg = P.Config(S=2, W=2, W_store=4, anchor=1, n_chunk=6, F=3, Hh=4, Ww=6,
+                   n_heads=2, head_dim=64, n_layers=1, mask=0)
+    rng = np.random.default_rng(23)
+    cache = {}
+
+    def raw(rnd, layer, cell, name):
+        key = (rnd, layer, cell, name)
+        if key not in cache:
+            cache[key] = rng.standard_normal((72, 2, 64))
+        return cache[key]
+
+    k, pages = 5, {}
+    for stage in range(cfg.S + 1):
+        a = R.group_output(cfg, k, stage, 0, raw, fp8=fp8, pages=pages)
+        b = R.group_output(cfg, k, stage, 0, raw, fp8=fp8)
+        assert np.array_equal(a, b)
+    assert len(pages) > 0

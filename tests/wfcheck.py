@@ -387,6 +387,7 @@ def check_attention(ro, k, layer, rows=None, heads=None, stages=None, seed=0, de
     worst = 0.0
     rng = np.random.default_rng([seed, k, layer])
     flips_of = {}
+    pages_of = {}          # (page reading) -> the oracle's pages of this round and layer
 
     def page_flips(kind, chunk, hs):
         """key_flips of one context page (all selected heads), once per call."""
@@ -405,7 +406,8 @@ def check_attention(ro, k, layer, rows=None, heads=None, stages=None, seed=0, de
             r = np.sort(rng.choice(s.N, size=min(rows, s.N), replace=False))
             r[-1] = s.N - 1           # always include the ragged tail row
         fp8 = {wf.WF_FP8: True, wf.WF_FP8K: "k"}.get(w.dtype, False)
-        want = WR.group_output(oc, k, st, layer, ro.raw, rows=r, heads=heads, fp8=fp8)
+        pages = pages_of.setdefault(fp8, {})
+        want = WR.group_output(oc, k, st, layer, ro.raw, rows=r, heads=heads, fp8=fp8, pages=pages)
         got = to64(s.bufs["out"][layer, st])
         if r is not None:
             got = got[r]
@@ -418,7 +420,7 @@ def check_attention(ro, k, layer, rows=None, heads=None, stages=None, seed=0, de
             qr = WR.q_rot(oc, k, st, layer, ro.raw)
             if r is not None:
                 qr = qr[r]
-            kk, vv = WR.group_keys(oc, k, st, layer, ro.raw, hs)
+            kk, vv = WR.group_keys(oc, k, st, layer, ro.raw, hs, pages=pages)
             tol = np.empty_like(err)
             for hi, h in enumerate(hs):
                 tol[:, hi, :] = bf16_attention_tolerance(qr[:, h, :], kk[:, hi, :], vv[:, hi, :],
@@ -434,7 +436,7 @@ def check_attention(ro, k, layer, rows=None, heads=None, stages=None, seed=0, de
             qr = WR.q_rot(oc, k, st, layer, ro.raw)
             if r is not None:
                 qr = qr[r]
-            kk, vv = WR.group_keys(oc, k, st, layer, ro.raw, hs, fp8=fp8)
+            kk, vv = WR.group_keys(oc, k, st, layer, ro.raw, hs, fp8=fp8, pages=pages)
             dk = np.concatenate([page_flips(kind, chunk, hs)
                                  for kind, chunk, _slot in P.key_entries(oc, k, st)], axis=0)
             # weights rounded to E4M3 (FP8) or bf16 (FP8K); the output is
