@@ -255,3 +255,20 @@ def test_full_size_wan13b_one_layer_fp8k_sampled():
         _log(f"{w.name}: worst err/bound {worst:.3f}")
     finally:
         s.close()
+
+
+def test_fp32_rounds_have_no_block():
+    """An fp32 handle (bound on the GPU) rejects the block before any
+    device work: WF_EUNSUPPORTED, with the reason in wf_last_error."""
+    from chunk_causal_dit_round_amd.workloads import TINY_FP32
+    s = Session(TINY_FP32.config(), io=False)
+    try:
+        fake = 1 << 20                      # never dereferenced: rejected first
+        dc = wf.make_dit_config(64)
+        names = [n for n, _ in wf.wf_dit_weights._fields_]
+        W = wf.make_dit_weights([{n: fake for n in names}])
+        st = wf.status_of(wf.wf_dit_layer, s.h, s.plan(0), 0, dc, W[0], fake, fake, fake, 1 << 30)
+        assert st == wf.WF_EUNSUPPORTED
+        assert "fp32" in wf.wf_last_error()
+    finally:
+        s.close()
