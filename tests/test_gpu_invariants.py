@@ -7,6 +7,7 @@
   long as every attention runs after its layer's publish.
 * Stale slots: slots a round neither reads nor writes may hold anything
   (NaN here) without touching the outputs.
+* HIP graphs: a round's layers captured into a graph replay to the eager bits.
 """
 
 import gc
@@ -131,5 +132,49 @@ def test_order_errors_on_device():
         assert wf.status_of(s.publish, s.plan(2), 0) == wf.WF_EORDER
         assert s.next_round() == 1
         torch.cuda.synchronize()
+    finally:
+        ro.close()
+
+
+@pytest.mark.parametrize("dtype", [wf.WF_BF16, wf.WF_FP8K], ids=["bf16", "fp8k"])
+def test_round_layers_replay_in_a_hip_graph(dtype):
+    """The layers of a round (publish + attention per layer) captured into
+    a HIP graph: every replay, with eager work and synchronisations between
+    replays, gives the bits the eager calls gave.  The library enqueues only
+    kernels on the caller's stream (no allocation, no memset), so the round
+    can sit inside a caller's graph."""
+    w = W_INV.with_(name=f"graph_{dtype}", dtype=dtype)
+    ro = Rollout(w)
+    s = ro.sess
+    try:
+        k_cap = 7                                   # steady: anchor, history, all stages
+        for k in range(k_cap):
+            ro.run(k)
+        ro.fill(k_cap)
+        plan = s.plan(k_cap)
+
+        def layers():
+            for layer in range(w.n_layers):
+                s.publish(plan, layer)
+                s.attention(plan, layer)
+
+        layers()                                    # eager
+        torch.cuda.synchronize()
+        eager_out = s.bufs["out"].clone()
+        eager_q = s.bufs["q_rot"].clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            layers()
+        torch.cuda.synchronize()
+        for rep in range(3):
+            s.bufs["out"].zero_()
+            s.bufs["q_rot"].fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(s.bufs["out"], eager_out), rep
+            assert torch.equal(s.bufs["q_rot"], eager_q), rep
+        s.commit(plan)
+        ro.run(k_cap + 1)                           # the handle carries on normally
     finally:
         ro.close()
