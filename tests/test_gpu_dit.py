@@ -272,3 +272,44 @@ def test_fp32_rounds_have_no_block():
         assert "fp32" in wf.wf_last_error()
     finally:
         s.close()
+
+
+def test_dit_layers_replay_in_a_hip_graph():
+    """Every layer of a round through the block (norm kernels, hipBLASLt
+    products, publish, attention) captured into a HIP graph: each replay
+    from the same residual stream gives the eager bits."""
+    w, ffn = SMALL[1]
+    s = Session(w.config(), io=False)
+    ds = DitSession(s, ffn, tag=w.name + "_graph")
+    try:
+        k_cap = 6
+        for k in range(k_cap):
+            plan = s.plan(k)
+            ds.load_x0(k)
+            ds.round(plan)
+        plan = s.plan(k_cap)
+        ds.load_x0(k_cap)
+        x_in = ds.x.clone()
+
+        def layers():
+            for layer in range(w.n_layers):
+                ds.layer(plan, layer)
+
+        layers()                                    # eager (also makes the product plans)
+        torch.cuda.synchronize()
+        eager = ds.x.clone()
+        ds.x.copy_(x_in)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            layers()
+        torch.cuda.synchronize()
+        for rep in range(3):
+            ds.x.copy_(x_in)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(ds.x, eager), rep
+        s.commit(plan)
+    finally:
+        s.close()
