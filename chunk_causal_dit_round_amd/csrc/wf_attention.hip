@@ -48,6 +48,7 @@
 #include <type_traits>
 
 #include "wf_kernels.h"
+#include "wf_partial.h"
 
 namespace wf {
 namespace {
@@ -432,8 +433,13 @@ __global__ __launch_bounds__(512, 1) void wf_attention_bf16_kernel(const AttnArg
   }
   if (pgroup == 0) __syncthreads();
 
-  // ---- epilogue: O = (O^T)^T / l ----
-  const float inv = 1.f / pair_sum32(l_run);
+  // ---- epilogue: O = (O^T)^T / l, or the half's partial result ----
+  const float l_sum = pair_sum32(l_run);
+  if (G.part >= 0) {
+    if (q < N) store_partial(a, G.part, q, h, -moff[0], l_sum, oacc, half);
+    return;
+  }
+  const float inv = 1.f / l_sum;
   if (q < N) {
     __bf16* orow = static_cast<__bf16*>(a.out) +
                    ((static_cast<int64_t>(G.stage) * N + q) * H + h) * D;
@@ -560,7 +566,54 @@ __global__ __launch_bounds__(kF32Threads) void wf_attention_f32_kernel(const Att
   }
 }
 
+// ------------------------------------------------------------ combine ----
+// Merges the two halves of each split group into the bf16 output: one thread
+// per 8 dims of one (row, head).  Exact softmax merge: with M = max(e_a, e_b)
+// and w = 2^(e - M), O = (O_a w_a + O_b w_b) / (l_a w_a + l_b w_b).
+constexpr int kCombineThreads = 256;
+
+__global__ __launch_bounds__(kCombineThreads) void wf_combine_kernel(const CombineArgs a) {
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const int chunks = a.D / 8;
+  const int64_t per_split = static_cast<int64_t>(a.N) * a.H * chunks;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * kCombineThreads + threadIdx.x;
+  if (idx >= per_split * a.n_split) return;
+  const int sp = static_cast<int>(idx / per_split);
+  const int64_t rem = idx - sp * per_split;
+  const int64_t rh = rem / chunks;                  // row * H + head
+  const int c = static_cast<int>(rem - rh * chunks);
+  const int64_t nh = static_cast<int64_t>(a.N) * a.H;
+  const int64_t ra = (2 * sp) * nh + rh, rb = ra + nh;
+  const float2 ea = reinterpret_cast<const float2*>(a.part_el)[ra];
+  const float2 eb = reinterpret_cast<const float2*>(a.part_el)[rb];
+  const float m = fmaxf(ea.x, eb.x);
+  const float wa = __builtin_amdgcn_exp2f(ea.x - m), wb = __builtin_amdgcn_exp2f(eb.x - m);
+  const float inv = 1.f / (ea.y * wa + eb.y * wb);
+  const float* oa = a.part_o + ra * a.D + 8 * c;
+  const float* ob = a.part_o + rb * a.D + 8 * c;
+  bf16x8 r;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const f32x4 xa = *reinterpret_cast<const f32x4*>(oa + 4 * k);
+    const f32x4 xb = *reinterpret_cast<const f32x4*>(ob + 4 * k);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[4 * k + j] = static_cast<__bf16>((xa[j] * wa + xb[j] * wb) * inv);
+  }
+  __bf16* orow = static_cast<__bf16*>(a.out) + (static_cast<int64_t>(a.stage[sp]) * nh + rh) * a.D;
+  *reinterpret_cast<bf16x8*>(orow + 8 * c) = r;
+}
+
 }  // namespace
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
+  if (a.n_split <= 0) return hipSuccess;
+  if (a.D % 8 != 0 || a.n_split > kMaxSplit) return hipErrorInvalidValue;
+  const int64_t threads = static_cast<int64_t>(a.n_split) * a.N * a.H * (a.D / 8);
+  const int64_t blocks = (threads + kCombineThreads - 1) / kCombineThreads;
+  hipLaunchKernelGGL(wf_combine_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kCombineThreads), 0,
+                     stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_attention(const AttnArgs& a, int dtype, hipStream_t stream) {
   if (a.n_items <= 0) return hipSuccess;

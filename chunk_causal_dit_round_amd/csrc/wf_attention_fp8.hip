@@ -41,6 +41,7 @@
 #include <cstdint>
 
 #include "wf_kernels.h"
+#include "wf_partial.h"
 
 namespace wf {
 namespace {
@@ -377,7 +378,11 @@ __global__ __launch_bounds__(kNT, 1) void wf_attention_fp8_kernel(const AttnArgs
     __builtin_amdgcn_sched_barrier(0); __syncthreads(); __builtin_amdgcn_sched_barrier(0);
   }
 
-  // ---- epilogue: O = (O^T)^T / l ----
+  // ---- epilogue: O = (O^T)^T / l, or the half's partial result ----
+  if (G.part >= 0) {
+    if (q < N) store_partial(a, G.part, q, h, -moff[0], lacc[0], oacc, half);
+    return;
+  }
   const float inv = 1.f / lacc[0];
   if (q < N) {
     __bf16* orow = static_cast<__bf16*>(a.out) + ((static_cast<int64_t>(G.stage) * N + q) * H + h) * kD;

@@ -38,6 +38,7 @@
 #include <cstdint>
 
 #include "wf_kernels.h"
+#include "wf_partial.h"
 
 namespace wf {
 namespace {
@@ -451,8 +452,13 @@ __global__ __launch_bounds__(kNT, 1) void wf_attention_fp8k_kernel(const AttnArg
   }
   if (pgroup == 0) __syncthreads();
 
-  // ---- epilogue: O = (O^T)^T / l ----
-  const float inv = 1.f / pair_sum32(l_run);
+  // ---- epilogue: O = (O^T)^T / l, or the half's partial result ----
+  const float l_sum = pair_sum32(l_run);
+  if (G.part >= 0) {
+    if (q < N) store_partial(a, G.part, q, h, -moff[0], l_sum, oacc, half);
+    return;
+  }
+  const float inv = 1.f / l_sum;
   if (q < N) {
     __bf16* orow = static_cast<__bf16*>(a.out) + ((static_cast<int64_t>(G.stage) * N + q) * H + h) * kD;
 #pragma unroll

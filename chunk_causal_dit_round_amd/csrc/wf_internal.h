@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <map>
 #include <string>
 #include <vector>
 
@@ -26,6 +27,11 @@ struct wf_handle {
   bool bound = false;
   std::vector<uint8_t> published;  // per layer, current round
   wf::DitState* dit = nullptr;
+  // Attention work split (wf_set_attention_split): compute units of the bound
+  // device, the mode, and the split chosen per list of group page counts.
+  int n_cu = 256;
+  int split_mode = WF_SPLIT_AUTO;
+  std::map<std::vector<int>, std::vector<int>> split_cache;
 };
 
 namespace wf {

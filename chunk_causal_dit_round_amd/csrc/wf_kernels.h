@@ -8,6 +8,7 @@
 #include <cstdint>
 
 #include "wf.h"
+#include "wf_plan.h"
 
 namespace wf {
 
@@ -48,6 +49,8 @@ struct AttnGroup {
   int32_t stage;     // query rows come from q_rot[stage]
   int32_t n_pages;   // key pages in context order
   int32_t item0;     // first work item of this group
+  int32_t part;      // -1: whole context, O goes to out; else the partial
+                     // result slot (O unnormalised, exponent offset, l)
   uint16_t slot[WF_MAX_PAGES];
 };
 
@@ -64,7 +67,21 @@ struct AttnArgs {
   int32_t n_items;     // sum over groups of H * q_tiles
   int32_t Npad, T;     // FP8 pages: tokens padded to 64 T, T tiles
   int32_t pad_;
-  AttnGroup grp[WF_MAX_GROUPS];
+  float* part_o;       // [kMaxSplit * 2][N][H][D] partial O (unnormalised)
+  float* part_el;      // [kMaxSplit * 2][N][H][2] (exponent offset e, l)
+  AttnGroup grp[WF_MAX_GROUPS + kMaxSplit];
+};
+
+// A split group's two halves (pages [0, n/2) and [n/2, n)) run as separate
+// work items that leave partial results; the combine kernel merges them:
+// with M = max(e_a, e_b), w = 2^(e - M), O = (O_a w_a + O_b w_b) / (l_a w_a + l_b w_b).
+struct CombineArgs {
+  const float* part_o;
+  const float* part_el;
+  void* out;           // [S+1][N][H][D] bf16
+  int32_t N, H, D;
+  int32_t n_split;
+  int32_t stage[kMaxSplit];
 };
 
 // Query rows per work item of each attention instance.
@@ -79,5 +96,6 @@ hipError_t launch_publish(const PublishArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_attention(const AttnArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_attention_fp8(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attention_fp8k(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 
 }  // namespace wf

@@ -116,9 +116,18 @@ uint64_t config_hash(const wf_config& c) {
 
 size_t pool_bytes(const Shape& sh) { return size_t(sh.L) * sh.n_slots * sh.page_bytes; }
 size_t anchor_bytes(const Shape& sh) { return size_t(sh.L) * sh.anchor_page_bytes; }
-size_t table_bytes(const Shape& sh) {
+size_t rope_table_bytes(const Shape& sh) {
   return (size_t(sh.n_frames) * sh.nt + size_t(sh.Hh) * sh.nh + size_t(sh.Ww) * sh.nw) *
          2 * sizeof(float);
+}
+// Two halves per split group: O [N][H][D] and (e, l) [N][H] in fp32.
+size_t split_scratch_bytes(const Shape& sh) {
+  if (sh.dtype == WF_F32) return 0;
+  const size_t nh = size_t(sh.N) * size_t(sh.H);
+  return size_t(kMaxSplit) * 2 * (nh * size_t(sh.D) + 2 * nh) * sizeof(float);
+}
+size_t table_bytes(const Shape& sh) {
+  return (rope_table_bytes(sh) + 255) / 256 * 256 + split_scratch_bytes(sh);
 }
 
 void build_plan(const Shape& sh, uint64_t hash, int64_t k, wf_plan* p) {

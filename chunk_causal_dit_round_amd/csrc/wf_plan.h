@@ -56,9 +56,17 @@ inline int slot_denoise(const Shape& sh, int64_t k, int j) {
   return 2 + sh.ring + static_cast<int>(k & 1) * sh.S + j;
 }
 
-// Bytes of caller buffers.
+// At most this many query groups of one attention launch are split into two
+// halves over their pages (bf16, FP8 and FP8K rounds); the halves' partial
+// results live in device scratch after the RoPE tables.
+constexpr int kMaxSplit = 2;
+
+// Bytes of caller buffers.  The table buffer holds the RoPE tables
+// (rope_table_bytes, rounded up to 256) and then the split scratch.
 size_t pool_bytes(const Shape& sh);
 size_t anchor_bytes(const Shape& sh);
+size_t rope_table_bytes(const Shape& sh);
+size_t split_scratch_bytes(const Shape& sh);
 size_t table_bytes(const Shape& sh);
 
 }  // namespace wf

@@ -8,6 +8,8 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <functional>
+#include <queue>
 #include <string>
 #include <vector>
 
@@ -127,6 +129,85 @@ wf_status do_publish(wf_handle* h, const wf_plan& p, int layer, const void* q, c
   return ok();
 }
 
+// Model of one attention launch: work-groups taken longest first by n_cu
+// compute units, one at a time each; a work-group over p pages costs its key
+// tiles plus a fixed 2 (query load, epilogue).  Returns the end time in tiles.
+double launch_end(const wf::Shape& sh, int n_cu, int per_group, const std::vector<int>& pages) {
+  std::vector<int> len(pages);
+  std::sort(len.begin(), len.end(), std::greater<int>());
+  std::priority_queue<double, std::vector<double>, std::greater<double>> free_at;
+  for (int i = 0; i < n_cu; ++i) free_at.push(0.0);
+  double end = 0.0;
+  for (const int p : len) {
+    const double tiles = (sh.dtype == WF_BF16 ? std::ceil(double(p) * sh.N / 64.0) : double(p) * sh.T) + 2.0;
+    for (int i = 0; i < per_group; ++i) {
+      const double t = free_at.top() + tiles;
+      free_at.pop();
+      free_at.push(t);
+      end = std::max(end, t);
+    }
+  }
+  return end;
+}
+
+// Stages of the groups to split (at most kMaxSplit), for the handle's mode.
+std::vector<int> choose_split(wf_handle* h, const wf_plan& p, const std::vector<int>& active) {
+  const wf::Shape& sh = h->sh;
+  std::vector<int> none;
+  if (sh.dtype == WF_F32 || h->split_mode == WF_SPLIT_OFF) return none;
+  std::vector<int> cand;   // splittable groups, longest first (ties: lower stage)
+  for (const int s : active)
+    if (p.groups[s].n_pages >= 2) cand.push_back(s);
+  std::stable_sort(cand.begin(), cand.end(),
+                   [&](int x, int y) { return p.groups[x].n_pages > p.groups[y].n_pages; });
+  if (h->split_mode == WF_SPLIT_FORCE) {
+    if (cand.size() > size_t(wf::kMaxSplit)) cand.resize(wf::kMaxSplit);
+    return cand;
+  }
+  std::vector<int> key;
+  for (const int s : active) key.push_back(p.groups[s].n_pages);
+  const auto hit = h->split_cache.find(key);
+  if (hit != h->split_cache.end()) return hit->second;
+
+  const int bm = sh.dtype == WF_BF16 ? wf::kAttnBM_bf16 : sh.dtype == WF_FP8 ? wf::kAttnBM_fp8 : wf::kAttnBM_fp8k;
+  const int per_group = sh.H * ((sh.N + bm - 1) / bm);
+  // The merge of one split group moves 10 N H D bytes (two fp32 partials in,
+  // bf16 out); priced at 5 TB/s against a tile of bm x 64 x D x 4 FLOP on
+  // one compute unit at 1.1 PFLOP/s over n_cu units, plus 2 tiles of launch gap.
+  const double tile_s = double(bm) * 64.0 * sh.D * 4.0 / (1.1e15 / h->n_cu);
+  const double merge = 2.0 + 10.0 * double(sh.N) * sh.H * sh.D / 5e12 / tile_s;
+  auto cost = [&](const std::vector<int>& sp) {
+    std::vector<int> pages;
+    for (const int s : active) {
+      const int n = p.groups[s].n_pages;
+      if (std::find(sp.begin(), sp.end(), s) == sp.end()) {
+        pages.push_back(n);
+      } else {
+        pages.push_back(n / 2);
+        pages.push_back(n - n / 2);
+      }
+    }
+    return launch_end(sh, h->n_cu, per_group, pages) + merge * double(sp.size());
+  };
+  std::vector<int> best;
+  double best_cost = cost(best);
+  for (size_t i = 0; i < cand.size(); ++i) {
+    const std::vector<int> one{cand[i]};
+    const double c1 = cost(one);
+    if (c1 < best_cost) best_cost = c1, best = one;
+  }
+  if (wf::kMaxSplit >= 2) {
+    for (size_t i = 0; i < cand.size(); ++i)
+      for (size_t j = i + 1; j < cand.size(); ++j) {
+        const std::vector<int> two{cand[i], cand[j]};
+        const double c2 = cost(two);
+        if (c2 < best_cost) best_cost = c2, best = two;
+      }
+  }
+  h->split_cache.emplace(key, best);
+  return best;
+}
+
 wf_status do_attention(wf_handle* h, const wf_plan& p, int layer, const void* q_rot, void* out,
                        hipStream_t stream) {
   const wf::Shape& sh = h->sh;
@@ -147,30 +228,66 @@ wf_status do_attention(wf_handle* h, const wf_plan& p, int layer, const void* q_
                  : sh.dtype == WF_FP8K ? wf::kAttnBM_fp8k
                                        : wf::kAttnBM_f32;
   a.q_tiles = (sh.N + bm - 1) / bm;
-  // Active groups, longest context first (ties: lower stage first).
-  int order[WF_MAX_GROUPS];
-  int ng = 0;
+  const int per_group = sh.H * a.q_tiles;
+  std::vector<int> active;
   for (int s = 0; s <= sh.S; ++s)
-    if (p.groups[s].n_pages > 0) order[ng++] = s;
-  std::stable_sort(order, order + ng,
-                   [&](int x, int y) { return p.groups[x].n_pages > p.groups[y].n_pages; });
+    if (p.groups[s].n_pages > 0) active.push_back(s);
+  const std::vector<int> split = choose_split(h, p, active);
+
+  // Runs of the launch: whole groups, or the two halves of a split group
+  // (pages [0, n/2) and [n/2, n)), longest first (ties: lower stage first).
+  struct Run {
+    int stage, page0, n_pages, part;
+  };
+  std::vector<Run> runs;
+  wf::CombineArgs c{};
+  for (const int s : active) {
+    const int n = p.groups[s].n_pages;
+    const auto it = std::find(split.begin(), split.end(), s);
+    if (it == split.end()) {
+      runs.push_back({s, 0, n, -1});
+    } else {
+      const int i = static_cast<int>(it - split.begin());
+      runs.push_back({s, 0, n / 2, 2 * i});
+      runs.push_back({s, n / 2, n - n / 2, 2 * i + 1});
+      c.stage[i] = s;
+    }
+  }
+  std::stable_sort(runs.begin(), runs.end(), [](const Run& x, const Run& y) { return x.n_pages > y.n_pages; });
   int item = 0;
-  for (int i = 0; i < ng; ++i) {
-    const wf_group& g = p.groups[order[i]];
+  for (size_t i = 0; i < runs.size(); ++i) {
+    const Run& r = runs[i];
+    const wf_group& g = p.groups[r.stage];
     wf::AttnGroup& o = a.grp[i];
     o.stage = g.stage;
-    o.n_pages = g.n_pages;
+    o.n_pages = r.n_pages;
     o.item0 = item;
-    for (int j = 0; j < g.n_pages; ++j) o.slot[j] = static_cast<uint16_t>(g.slot[j]);
-    item += sh.H * a.q_tiles;
+    o.part = r.part;
+    for (int j = 0; j < r.n_pages; ++j) o.slot[j] = static_cast<uint16_t>(g.slot[r.page0 + j]);
+    item += per_group;
   }
-  a.n_groups = ng;
+  a.n_groups = static_cast<int>(runs.size());
   a.n_items = item;
+  char* scratch = static_cast<char*>(h->tables) + (wf::rope_table_bytes(sh) + 255) / 256 * 256;
+  const size_t nhd = size_t(sh.N) * size_t(sh.H) * size_t(sh.D);
+  a.part_o = reinterpret_cast<float*>(scratch);
+  a.part_el = reinterpret_cast<float*>(scratch + size_t(wf::kMaxSplit) * 2 * nhd * sizeof(float));
   (void)hipGetLastError();
-  const hipError_t e = sh.dtype == WF_FP8    ? wf::launch_attention_fp8(a, stream)
-                       : sh.dtype == WF_FP8K ? wf::launch_attention_fp8k(a, stream)
-                                             : wf::launch_attention(a, sh.dtype, stream);
+  hipError_t e = sh.dtype == WF_FP8    ? wf::launch_attention_fp8(a, stream)
+                 : sh.dtype == WF_FP8K ? wf::launch_attention_fp8k(a, stream)
+                                       : wf::launch_attention(a, sh.dtype, stream);
   if (e != hipSuccess) return fail(WF_EDEVICE, std::string("attention launch: ") + hipGetErrorString(e));
+  if (!split.empty()) {
+    c.part_o = a.part_o;
+    c.part_el = a.part_el;
+    c.out = out;
+    c.N = sh.N;
+    c.H = sh.H;
+    c.D = sh.D;
+    c.n_split = static_cast<int>(split.size());
+    e = wf::launch_combine(c, stream);
+    if (e != hipSuccess) return fail(WF_EDEVICE, std::string("combine launch: ") + hipGetErrorString(e));
+  }
   return ok();
 }
 
@@ -247,7 +364,7 @@ wf_status wf_bind(wf_handle* h, void* d_pool, size_t pool_bytes, void* d_anchor_
   if (sup != WF_OK) return sup;
 
   // cos/sin of every (position, pair) per axis, computed in fp64.
-  std::vector<float> tab(wf::table_bytes(sh) / sizeof(float));
+  std::vector<float> tab(wf::rope_table_bytes(sh) / sizeof(float));
   size_t at = 0;
   auto axis = [&](int n_pos, int n_pairs) {
     for (int pos = 0; pos < n_pos; ++pos) {
@@ -264,10 +381,23 @@ wf_status wf_bind(wf_handle* h, void* d_pool, size_t pool_bytes, void* d_anchor_
   axis(sh.Ww, sh.nw);
   const hipError_t e = hipMemcpy(d_tables, tab.data(), tab.size() * sizeof(float), hipMemcpyHostToDevice);
   if (e != hipSuccess) return fail(WF_EDEVICE, std::string("table upload: ") + hipGetErrorString(e));
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+    h->n_cu = cus;
+  h->split_cache.clear();
   h->pool = d_pool;
   h->anchor = d_anchor_raw;
   h->tables = d_tables;
   h->bound = true;
+  return ok();
+}
+
+wf_status wf_set_attention_split(wf_handle* h, int32_t mode) {
+  if (!h) return fail(WF_EINVAL, "handle is NULL");
+  if (mode != WF_SPLIT_AUTO && mode != WF_SPLIT_OFF && mode != WF_SPLIT_FORCE)
+    return fail(WF_EINVAL, "unknown split mode " + std::to_string(mode));
+  h->split_mode = mode;
   return ok();
 }
 

@@ -18,6 +18,7 @@ WF_MAX_PAGES = 48
 WF_OK, WF_EINVAL, WF_ERANGE, WF_EORDER, WF_ESMALL, WF_EDEVICE, WF_EUNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
 WF_F32, WF_BF16, WF_FP8, WF_FP8K = 0, 1, 2, 3
 WF_MASK_WAVE, WF_MASK_ROLLING = 0, 1
+WF_SPLIT_AUTO, WF_SPLIT_OFF, WF_SPLIT_FORCE = 0, 1, 2
 WF_KIND_ANCHOR, WF_KIND_HISTORY, WF_KIND_STORE, WF_KIND_DENOISE = 0, 1, 2, 3
 
 i32, i64, u64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_double
@@ -89,6 +90,7 @@ def _load():
         "wf_reset": (i32, [H]),
         "wf_kv_publish": (i32, [H, ctypes.POINTER(wf_plan), i32, cvp, cvp, cvp, vp, vp]),
         "wf_wave_attention": (i32, [H, ctypes.POINTER(wf_plan), i32, cvp, vp, vp]),
+        "wf_set_attention_split": (i32, [H, i32]),
         "wf_round_commit": (i32, [H, ctypes.POINTER(wf_plan)]),
         "wf_round": (i32, [H, ctypes.POINTER(wf_plan), cvp, cvp, cvp, vp, vp, vp]),
         "wf_dit_workspace_bytes": (i32, [H, ctypes.POINTER(wf_dit_config), ctypes.POINTER(sz)]),
@@ -195,6 +197,10 @@ def wf_kv_publish(h, plan, layer, q, k, v, q_rot, stream=None):
 def wf_wave_attention(h, plan, layer, q_rot, out, stream=None):
     _check(_lib.wf_wave_attention(h, ctypes.byref(plan), layer, _ptr(q_rot), _ptr(out),
                                   _stream(stream)))
+
+
+def wf_set_attention_split(h, mode):
+    _check(_lib.wf_set_attention_split(h, mode))
 
 
 def wf_round_commit(h, plan):

@@ -48,7 +48,10 @@
  *                         page_elems = 2 * H * N * D.
  *   pool                  [L][n_slots] pages, n_slots = 4 + max(W, W_store) + 2 S.
  *   anchor_raw            [L] pages holding chunk 0's unrotated K and its Vt.
- *   tables                fp32 cos/sin pairs written by wf_bind.
+ *   tables                fp32 cos/sin pairs written by wf_bind, rounded up to
+ *                         256 bytes, then (bf16, FP8, FP8K) the attention's
+ *                         split scratch: 4 x ([N][H][D] + [N][H][2]) fp32,
+ *                         the partial results of at most two split groups.
  *
  * FP8 pages (dtype WF_FP8; WF App. C.6 Eq. 20-21: K/V in 8 bits halve the
  * payload).  q, k, v, q_rot, out and anchor_raw are bf16 as above; a pool
@@ -118,6 +121,12 @@ typedef enum {
   WF_MASK_ROLLING = 1  /* every active denoising chunk reads every other one
                           (Rolling Forcing's window, WF §3.1; comparison only) */
 } wf_mask;
+
+typedef enum {
+  WF_SPLIT_AUTO = 0,   /* split groups when the launch's modelled time drops  */
+  WF_SPLIT_OFF = 1,    /* every group is one run over its whole context       */
+  WF_SPLIT_FORCE = 2   /* always split the two longest groups (>= 2 pages)    */
+} wf_split_mode;
 
 typedef enum {
   WF_KIND_ANCHOR = 0,  /* first clean chunk, persistent            (App. B.3) */
@@ -250,6 +259,22 @@ wf_status wf_kv_publish(wf_handle* h, const wf_plan* plan, int32_t layer,
  * WF_EORDER if this layer was not published in this round. */
 wf_status wf_wave_attention(wf_handle* h, const wf_plan* plan, int32_t layer,
                             const void* d_q_rot, void* d_out, void* stream);
+
+/* How wf_wave_attention divides its work (bf16, FP8 and FP8K rounds; fp32
+ * rounds never split).  A launch runs one work-group per (group, head, 256
+ * query rows), each over the group's whole context, so the launch ends with
+ * a tail in which the shortest groups' work-groups leave compute units idle.
+ * A split group instead runs as two halves over pages [0, n/2) and [n/2, n)
+ * of its context; each half leaves its unnormalised output, exponent offset
+ * and weight sum in the split scratch (see "tables" above), and a second
+ * launch merges the two softmax partials exactly (WF §4.2 gives the per-
+ * stage key counts that make the groups' lengths unequal).  WF_SPLIT_AUTO
+ * (the default) models the launch as work-groups taken longest first by
+ * the device's compute units and splits the at most two groups that
+ * minimise that model's end time plus the merge; the choice is cached per
+ * list of group lengths.  Results of the modes agree up to rounding.
+ * WF_EINVAL for a NULL handle or an unknown mode.  Host only. */
+wf_status wf_set_attention_split(wf_handle* h, int32_t mode);
 
 /* End the round (WF App. B.3): requires every layer published; advances
  * the expected round.  Host only: the store page is promoted in place. */

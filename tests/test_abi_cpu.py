@@ -32,7 +32,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     assert {"wf_dit_workspace_bytes", "wf_dit_layer", "wf_dit_round"} <= set(names)
     lib = ctypes.CDLL(wf.LIB_PATH)
     for n in names:
@@ -84,7 +84,11 @@ def test_pool_bytes():
     page = 2 * 4680 * 12 * 128 * 2
     assert pool == 30 * 20 * page
     assert anc == 30 * page
-    assert tab == (133 * 3 * 22 + 30 * 21 + 52 * 21) * 8
+    rope = (133 * 3 * 22 + 30 * 21 + 52 * 21) * 8
+    nh = 4680 * 12
+    # RoPE tables rounded up to 256 bytes, then the split scratch: two split
+    # groups x two halves x (O [N][H][D] + (e, l) [N][H]) in fp32
+    assert tab == -(-rope // 256) * 256 + 2 * 2 * (nh * 128 + 2 * nh) * 4
 
 
 def test_pool_bytes_fp8():
@@ -258,3 +262,22 @@ def test_dit_workspace_bytes_and_errors_before_device_work():
         assert wf.status_of(wf.wf_dit_workspace_bytes, h, wf.make_dit_config(64)) == wf.WF_EUNSUPPORTED
     finally:
         wf.wf_destroy(h)
+
+
+def test_split_mode_checked_on_the_host():
+    h = wf.wf_create(WAN13B_4STEP.config())
+    try:
+        for mode in (wf.WF_SPLIT_OFF, wf.WF_SPLIT_FORCE, wf.WF_SPLIT_AUTO):
+            wf.wf_set_attention_split(h, mode)
+        assert wf.status_of(wf.wf_set_attention_split, h, 3) == wf.WF_EINVAL
+        assert wf.status_of(wf.wf_set_attention_split, h, -1) == wf.WF_EINVAL
+    finally:
+        wf.wf_destroy(h)
+    assert wf.status_of(wf.wf_set_attention_split, None, 0) == wf.WF_EINVAL
+
+
+def test_fp32_rounds_have_no_split_scratch():
+    from chunk_causal_dit_round_amd.workloads import TINY_FP32
+    _, _, tab = wf.wf_pool_bytes(TINY_FP32.config())
+    rope = (6 * 3 * 12 + 4 * 10 + 6 * 10) * 8    # 18 frames; 12, 10, 10 pairs of 64 dims
+    assert tab == -(-rope // 256) * 256

@@ -255,6 +255,50 @@ def test_full_size_wan13b_4step_fp8k_sampled():
         ro.close()
 
 
+SPLIT_CASES = [SMALL_BF16[0], SMALL_BF16[1], SMALL_BF16[2], SMALL_BF16[3], SMALL_FP8[0], SMALL_FP8[2],
+               SMALL_FP8K[0], SMALL_FP8K[2], SMALL_FP8K[3]]
+
+
+@pytest.mark.parametrize("w", SPLIT_CASES, ids=lambda w: w.name)
+def test_small_split_every_round(w):
+    """Every round with the two longest groups split into halves over their
+    pages (partial results merged by the combine kernel), against the oracle
+    at the same bars as the unsplit runs."""
+    _log(f"{w.name} split: {w.n_chunk + w.S} rounds")
+    ro = Rollout(w, split=wf.WF_SPLIT_FORCE)
+    worst = 0.0
+    try:
+        for k in range(w.n_chunk + w.S):
+            ro.run(k, mode="layers")
+            for layer in range(w.n_layers):
+                worst = max(worst, check_attention(ro, k, layer))
+    finally:
+        ro.close()
+    _log(f"  max abs err {worst:.3e}")
+
+
+def test_split_modes_agree_full_size_layer():
+    """1.3B steady round, one layer: the automatic split, no split and the
+    forced split give the same outputs up to fp32 merge rounding and the
+    bf16 rounding of the output (two bf16 units at most)."""
+    w = WAN13B_4STEP.with_(n_layers=1)
+    outs = {}
+    for mode in (wf.WF_SPLIT_OFF, wf.WF_SPLIT_AUTO, wf.WF_SPLIT_FORCE):
+        ro = Rollout(w, split=mode)
+        try:
+            for k in range(14):
+                ro.run(k)
+            outs[mode] = ro.sess.bufs["out"][0].float().clone()
+        finally:
+            ro.close()
+    ref = outs[wf.WF_SPLIT_OFF]
+    for mode in (wf.WF_SPLIT_AUTO, wf.WF_SPLIT_FORCE):
+        diff = (outs[mode] - ref).abs()
+        bound = 2 * 2.0 ** -8 * ref.abs() + 1e-3
+        _log(f"  mode {mode}: max |diff| {diff.max().item():.3e}")
+        assert bool((diff <= bound).all()), (mode, diff.max().item())
+
+
 class GrowingKeys(Rollout):
     """Keys of chunk i scaled by 1 + 0.8 i: along the context (anchor first,
     then history oldest first) a query row's running max keeps growing by

@@ -205,10 +205,12 @@ def oracle_cfg(w):
 class Rollout:
     """One request of workload ``w`` on the GPU, round by round."""
 
-    def __init__(self, w, device="cuda", gen_device=None, tag=None, perturb=None):
+    def __init__(self, w, device="cuda", gen_device=None, tag=None, perturb=None, split=None):
         self.w = w
         self.tag = tag or w.name
         self.sess = Session(w.config(), device=device)
+        if split is not None:
+            wf.wf_set_attention_split(self.sess.h, split)
         self.gen_device = gen_device or ("cpu" if w.n_tokens * w.n_heads * w.head_dim < 1 << 20
                                          else device)
         self.q_scale = synth.head_scales(w.n_heads, self.tag) if w.q_head_scale else None
