@@ -57,26 +57,30 @@ PEAK_HBM_GBPS = 8000.0
 CSRC = os.path.join(ROOT, "chunk_causal_dit_round_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
-# Attention instance per page type: peak, dtype label, kernel, its source and
-# the committed counter summary its HBM traffic comes from.
+# Attention instance per page type: peak, dtype label, kernel, its source, the
+# committed counter summary its HBM traffic comes from and the workload the
+# counters were taken on.
 PAGE_KINDS = {
     "bf16": dict(peak=PEAK_BF16_TFLOPS, dtype="bf16", kernel="wf_attention_bf16_kernel<128>",
                  src="wf_attention.hip", traffic="attention_bf16_wan1.3b_4step_hbm_traffic.txt",
-                 what="bf16 MFMA peak"),
+                 workload="wan1.3b_4step", what="bf16 MFMA peak"),
     "fp8": dict(peak=PEAK_FP8_TFLOPS, dtype="fp8", kernel="wf_attention_fp8_kernel",
                 src="wf_attention_fp8.hip",
                 traffic="attention_fp8_wan1.3b_4step_kernel_trace_and_traffic.txt",
-                what="fp8 MFMA peak (FP8 E4M3 pages)"),
+                workload="wan1.3b_4step_fp8", what="fp8 MFMA peak (FP8 E4M3 pages)"),
     "fp8k": dict(peak=PEAK_FP8K_TFLOPS, dtype="fp8 QK^T + bf16 PV", kernel="wf_attention_fp8k_kernel",
                  src="wf_attention_fp8k.hip",
                  traffic="attention_fp8k_wan1.3b_4step_kernel_trace_and_traffic.txt",
-                 what="blended fp8 / bf16 MFMA peak (8-bit-key pages: FP8 K, bf16 V)"),
+                 workload="wan1.3b_4step_fp8k", what="blended fp8 / bf16 MFMA peak (8-bit-key pages: FP8 K, bf16 V)"),
 }
 
 
-def measured_traffic(kind):
+def measured_traffic(kind, workload):
     """HBM bytes per attention launch from the committed counter summary, or
-    None if the kernel source changed since the counters were taken."""
+    None if the kernel source changed since the counters were taken or the
+    counters were taken on another workload."""
+    if workload != kind["workload"]:
+        return None
     try:
         fields = dict(line.split(":", 1) for line in open(os.path.join(PROFILES, kind["traffic"]))
                       if ":" in line)
@@ -463,7 +467,7 @@ def main():
                    "rounds_timed": [k0, k0 + args.steps - 1], "n_rounds": n_rounds},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak,
                      "unit": "TFLOP/s", "frac": achieved / peak,
-                     "traffic": measured_traffic(kind),
+                     "traffic": measured_traffic(kind, w.name),
                      "kernel": kind["kernel"],
                      "flops_per_launch": flops_launch, "avg_launch_ms": att_avg},
         "attention_tflops_round": total_flops / elapsed / 1e12,
