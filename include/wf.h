@@ -255,7 +255,9 @@ wf_status wf_kv_publish(wf_handle* h, const wf_plan* plan, int32_t layer,
 /* Layer `layer` of the round's attention (WF §3.1 Eq. 4-5): for every
  * active query group g and head, out = softmax(scale * Q K^T) V over the
  * group's key pages concatenated in plan order.  One launch covers all
- * groups.  d_q_rot: [S+1][N][H][D] from wf_kv_publish; d_out: [S+1][N][H][D].
+ * groups, followed by one merge launch when groups are split (see
+ * wf_set_attention_split).  d_q_rot: [S+1][N][H][D] from wf_kv_publish;
+ * d_out: [S+1][N][H][D].
  * WF_EORDER if this layer was not published in this round. */
 wf_status wf_wave_attention(wf_handle* h, const wf_plan* plan, int32_t layer,
                             const void* d_q_rot, void* d_out, void* stream);
