@@ -12,9 +12,7 @@
 //
 // bf16 instance (D = 64 or 128), CDNA4 MFMA v_mfma_f32_32x32x16_bf16:
 //   * work item = (group, head, 256 query rows); 8 waves x 32 queries, in two
-//     groups of 4 (waves i and i+4 share a SIMD).  A group the host splits
-//     runs as two halves over disjoint page ranges, each storing its
-//     unnormalised partial result for wf_combine_kernel (wf_partial.h).
+//     groups of 4 (waves i and i+4 share a SIMD).
 //   * S^T = K Q^T: A = 32 keys x 16 dims of K from LDS, B = Q fragments held
 //     in registers for the whole item.  Each lane ends up owning one query
 //     (its column), so the row max is an in-lane reduction plus one
