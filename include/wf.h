@@ -213,7 +213,8 @@ wf_status wf_create(const wf_config* cfg, wf_handle** out);
 void wf_destroy(wf_handle* h);
 
 /* Bytes the caller must allocate for the slot pool, the anchor store and
- * the RoPE tables of `cfg`.  Any output pointer may be NULL. */
+ * the RoPE tables of `cfg` (the table buffer also holds the attention's
+ * split scratch, see "tables" above).  Any output pointer may be NULL. */
 wf_status wf_pool_bytes(const wf_config* cfg, size_t* pool_bytes,
                         size_t* anchor_bytes, size_t* table_bytes);
 
