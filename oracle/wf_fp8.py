@@ -16,11 +16,11 @@ neither the FP8 format nor the scale granularity.  Readings taken here:
   block), and stores x / 2^e.
 * Blocks: every 64-token tile of one head of a page, separately for the
   rotated key (after RoPE) and for the value; pages hold ceil(N / 64) * 64
-  tokens, the padding tokens are zero and never attended.  Queries are
-  quantised per row (one token of one head): the bf16 rotated query row times
-  c = scale * log2(e), with c and the product in fp32 (the precision the
-  quantised codes are decided in), quantised, then divided by c again
-  (``fp8_query``).
+  tokens, the padding tokens are zero and never attended.
+* Queries: App. C.6 speaks of the K/V payload only and says nothing of the
+  query.  The plainest reading that keeps q_rot's bf16 layout is to quantise
+  each bf16 rotated query row (one token of one head) on its own, by the same
+  block rule with one exponent per row (``fp8_query``).
 * Attention over FP8 pages is the plain softmax attention of
   ``wf_attention.attend`` applied to the dequantised Q, K and V.
 
@@ -142,13 +142,11 @@ def fp8_rows(x: np.ndarray) -> np.ndarray:
     return out
 
 
-def fp8_query(q_bf16: np.ndarray, scale: float) -> np.ndarray:
-    """The query reading: rows of q (bf16 values) times c = fp32(scale *
-    log2 e), the product rounded to fp32, quantised per row, divided by c.
-    Equal to ``fp8_rows`` whenever c is a power of two."""
-    c = np.float32(scale * math.log2(math.e))
-    prod = (np.asarray(q_bf16, dtype=np.float32) * c).astype(np.float64)
-    return fp8_rows(prod) / np.float64(c)
+def fp8_query(q_bf16: np.ndarray) -> np.ndarray:
+    """The query reading: each row of q (bf16 values, [N, d]) quantised on
+    its own by the block rule (one power-of-two exponent per row), then
+    dequantised (fp64)."""
+    return fp8_rows(q_bf16)
 
 
 def bf16_round(x) -> np.ndarray:

@@ -105,8 +105,8 @@ def group_output(cfg: P.Config, k: int, stage: int, layer: int, raw,
     ``rows`` / ``heads`` select query tokens and heads (all by default);
     every selected row still attends to its full key list.  With ``fp8`` the
     pages are FP8 pages (``fp8="k"``: FP8 keys, exact values) and each
-    rotated query row, stored in bf16, is scaled and quantised per row (App.
-    C.6 reading, ``wf_fp8.fp8_query``).  ``pages`` as in ``group_keys``.
+    rotated query row, stored in bf16, is quantised per row (the query
+    reading of ``wf_fp8.fp8_query``).  ``pages`` as in ``group_keys``.
     """
     heads = list(range(cfg.n_heads)) if heads is None else list(heads)
     qr = q_rot(cfg, k, stage, layer, raw)
@@ -118,7 +118,7 @@ def group_output(cfg: P.Config, k: int, stage: int, layer: int, raw,
     for hi, h in enumerate(heads):
         qh = qr[:, h, :]
         if fp8:
-            qh = F8.fp8_query(F8.bf16_round(qh), sc)
+            qh = F8.fp8_query(F8.bf16_round(qh))
         out[:, hi, :] = attend(qh, kk[:, hi, :], vv[:, hi, :], sc)
     return out
 

@@ -169,7 +169,7 @@ def test_fp8_round_reduces_to_dense_attention_on_dequantised_inputs():
         ks.append(F.fp8_tiles(kr))
         vs.append(F.fp8_tiles(raw(rnd, 0, cell, "v")[:, 1, :]))
     q = rope3d(raw(k, 0, stage, "q"), 3 * (k - stage), 3, 4, 6, cfg.rope_theta)[:, 1, :]
-    q = F.fp8_query(F.bf16_round(q), 1 / math.sqrt(64))
+    q = F.fp8_query(F.bf16_round(q))
     ref = attend(q, np.concatenate(ks), np.concatenate(vs), 1 / math.sqrt(64))
     assert np.allclose(got[:, 0, :], ref, rtol=0, atol=1e-12)
     # and the FP8 result stays close to the exact one (quantisation only)
@@ -177,26 +177,36 @@ def test_fp8_round_reduces_to_dense_attention_on_dequantised_inputs():
     assert np.max(np.abs(got - exact)) < 0.1
 
 
-def test_query_reading_scales_before_quantising():
-    """fp8_query quantises the fp32 product q * c per row: when c is a power
-    of two it equals plain per-row quantisation; otherwise it is the
-    dequantised scaled row divided by c, within half an E4M3 ulp of q."""
+def _smallest_exponent_brute(amax):
+    """Smallest integer e with amax <= 448 * 2^e, by scanning (0 for 0)."""
+    if amax == 0:
+        return 0
+    e = -200
+    while amax > 448.0 * 2.0 ** e:
+        e += 1
+    return e
+
+
+def test_query_reading_is_torch_per_row_e4m3():
+    """fp8_query quantises every bf16 row on its own: divided by 2^e (e the
+    smallest integer with max |row| <= 448 * 2^e, found by scanning), cast
+    to torch's float8_e4m3fn (round to nearest even), cast back and
+    multiplied by 2^e.  Rows span magnitudes from 1e-6 to 1e5, so some
+    elements land in the subnormal range of their row's scale."""
     rng = np.random.default_rng(31)
-    q = F.bf16_round(rng.standard_normal((6, 128)))
-    log2e = math.log2(math.e)
-    for k in (-3, 0, 2):                     # c = 2^k exactly
-        scale = 2.0 ** k / log2e
-        assert np.float32(scale * log2e) == np.float32(2.0 ** k)
-        assert np.array_equal(F.fp8_query(q, scale), F.fp8_rows(q))
-    scale = 1 / math.sqrt(128)
-    c = float(np.float32(scale * log2e))
-    got = F.fp8_query(q, scale)
-    ref = F.fp8_rows((q.astype(np.float32) * np.float32(c)).astype(np.float64)) / c
-    assert np.array_equal(got, ref)
-    # within half an E4M3 ulp (relative 2^-4) plus the subnormal step of the row
-    amax = np.max(np.abs(q * c), axis=1, keepdims=True)
-    e = np.array([[F.pow2_exponent(a)] for a in amax[:, 0]])
-    assert np.all(np.abs(got - q) <= np.abs(q) * 2.0 ** -4 + 2.0 ** (e - 10) / c + 1e-12)
+    mags = np.exp2(rng.integers(-20, 17, 40)).astype(np.float64)
+    q = F.bf16_round(rng.standard_normal((40, 128)) * mags[:, None])
+    q[3, :] = 0.0                                     # an all-zero row
+    q[4, 5:] = q[4, 5:] * 2.0 ** -14                  # one large, many tiny
+    got = F.fp8_query(q)
+    for r in range(q.shape[0]):
+        e = _smallest_exponent_brute(float(np.max(np.abs(q[r]))))
+        x = torch.tensor(np.ldexp(q[r], -e), dtype=torch.float32)
+        ref = x.to(torch.float8_e4m3fn).to(torch.float64).numpy()
+        np.testing.assert_array_equal(got[r], np.ldexp(ref, e), err_msg=f"row {r}")
+    # the reading does not depend on the softmax scale: a row and the same
+    # row times a power of two quantise to the same codes
+    np.testing.assert_array_equal(F.fp8_query(q * 8.0), got * 8.0)
 
 
 def test_fp8_keys_only_round_is_dense_attention_with_exact_values():
@@ -227,7 +237,7 @@ def test_fp8_keys_only_round_is_dense_attention_with_exact_values():
         ks.append(F.fp8_tiles(kr))
         vs.append(raw(rnd, 0, cell, "v")[:, 0, :])
     q = rope3d(raw(k, 0, stage, "q"), 3 * (k - stage), 3, 4, 6, cfg.rope_theta)[:, 0, :]
-    q = F.fp8_query(F.bf16_round(q), 1 / math.sqrt(64))
+    q = F.fp8_query(F.bf16_round(q))
     ref = attend(q, np.concatenate(ks), np.concatenate(vs), 1 / math.sqrt(64))
     assert np.allclose(got[:, 0, :], ref, rtol=0, atol=1e-12)
     # values untouched: the keys-only page differs from the full FP8 page

@@ -5,10 +5,11 @@ and the fp32 rotation error bound against an fp32 rotation."""
 import math
 
 import numpy as np
+import pytest
 import torch
 
 from oracle import wf_fp8 as F8
-from wfcheck import _midpoint_distance, _rotation_error
+from wfcheck import _midpoint_distance, _query_term, _rotation_error, query_shift
 
 
 def _brute_margin(x, grid):
@@ -63,3 +64,50 @@ def test_rotation_error_bounds_an_fp32_rotation():
     a32, b32 = a.astype(np.float32), b.astype(np.float32)
     got = np.stack([a32 * c32 - b32 * s32, a32 * s32 + b32 * c32], 1).astype(np.float64)
     assert (np.abs(got - exact) <= _rotation_error(exact)).all()
+
+
+def _kernel_query(x, scale):
+    """The quantised query of the FP8 / 8-bit-key attention kernels as the
+    tolerance models it: y = fp32(x) * fp32(scale log2 e) in fp32, one
+    power-of-two exponent per row (the block rule on y), E4M3 by torch's
+    float8_e4m3fn, divided by c again (a model of the kernel's rounding,
+    used here only to check the bound that covers it)."""
+    c = np.float32(scale * math.log2(math.e))
+    y = (x.astype(np.float32) * c).astype(np.float64)
+    out = np.empty_like(y)
+    for r in range(y.shape[0]):
+        e = F8.pow2_exponent(np.max(np.abs(y[r])))
+        z = torch.tensor(np.ldexp(y[r], -e), dtype=torch.float32).to(torch.float8_e4m3fn)
+        out[r] = np.ldexp(z.to(torch.float64).numpy(), e) / float(c)
+    return out
+
+
+@pytest.mark.parametrize("n_keys,key_gain,q_gain", [(64, 1.0, 1.0), (360, 1.0, 1.0), (4096, 1.0, 1.0),
+                                                     (512, 3.0, 1.0), (256, 1.0, 4.0)])
+def test_query_term_bounds_the_grid_change(n_keys, key_gain, q_gain):
+    """The query term of ``fp8_attention_tolerance`` covers the change of
+    the exact attention output when the oracle's per-row quantised query
+    is replaced by the kernel's (quantised on the grid of q * scale log2 e):
+    same keys and values, exact fp64 softmax on both sides.  Peaky rows
+    (large key or query gain) and broad ones (4096 keys) are covered."""
+    from oracle.wf_attention import attend
+
+    rng = np.random.default_rng([7, n_keys])
+    d, nq, scale = 128, 48, 1 / math.sqrt(128)
+    q = rng.standard_normal((nq, d)) * q_gain
+    k = F8.fp8_tiles(rng.standard_normal((n_keys, d)) * key_gain)
+    v = rng.standard_normal((n_keys, d))
+    x = F8.bf16_round(q)
+    q8o = F8.fp8_query(x)
+    q8k = _kernel_query(x, scale)
+    assert not np.array_equal(q8o, q8k)          # the grids really differ
+    shift = np.abs(attend(q8k, k, v, scale) - attend(q8o, k, v, scale))
+    s = scale * (q8o @ k.T)
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    term = _query_term(p, k, v, p @ v, scale, query_shift(q, scale))
+    ratio = (shift / term).max()
+    assert ratio <= 1.0, ratio
+    # and the term is not vacuous: it stays within a small factor of the
+    # largest shift it has to cover
+    assert term.max() < 40 * shift.max()

@@ -93,21 +93,70 @@ def key_flips(ke):
     return np.where(near, step * sc, 0.0)[:n]
 
 
-def query_flips(q, q8, scale):
-    """Possible |q8 - q8_oracle| ([Nq, d]): the bf16 rounding of the exact
-    rotated query ``q`` can flip where it lies within the fp32 rotation
-    error of a bf16 midpoint, and then the row's E4M3 code of q times
-    scale * log2(e) may move one step."""
-    qdist, _ = _midpoint_distance(q, 7, -126)
-    qnear = (qdist > 0) & (qdist < _rotation_error(q))
-    c = scale * math.log2(math.e)
-    rows = np.abs(q8 * c).max(axis=1)
-    qsc = np.exp2(np.array([F8.pow2_exponent(r) for r in rows], dtype=np.float64))[:, None] / c
-    _, qstep = _midpoint_distance(q8 / qsc, 3, -6)
-    return np.where(qnear, qstep * qsc, 0.0)
+def query_shift(q, scale):
+    """How the kernel's quantised query row can differ from the oracle's
+    (``q`` [Nq, d]: the exact rotated query rows of one head).
+
+    The oracle quantises x = bf16(q) per row on the E4M3 grid of x itself
+    (``wf_fp8.fp8_query``).  The kernel quantises the fp32 product y = x c,
+    c = fp32(scale log2 e), per row on the E4M3 grid of y (the row exponent
+    eq = the smallest with max |y| <= 448 2^eq), so that Q K^T comes out in
+    the softmax's base-2 units; its query is Q(y) / c.  The two grids differ
+    by the factor c, which is no power of two, so the two rounding errors are
+    unrelated.  Per element, q8_gpu - q8_oracle = a + b + r with
+      * a = x - fp8_query(x), known exactly;
+      * b = one bf16 step where the kernel's fp32 rotation may round q to the
+        other bf16 neighbour (q within the rotation error of a bf16
+        midpoint), else 0;
+      * r = Q(y) / c - x, the kernel's own rounding: |r| <= h with h half the
+        E4M3 step of y's binade (2^(E - 4) for |y| in [2^E, 2^(E+1)); the
+        subnormal half step 2^(eq - 10) below 2^(eq - 6)), divided by c, plus
+        the fp32 roundings of y and of c (2^-23 |x|).
+    eq is taken for max |y| (1 + 2^-7), which covers a flipped row maximum.
+    Returns (a, b, h), each [Nq, d]."""
+    x = F8.bf16_round(q)
+    a = x - F8.fp8_query(x)
+    qdist, qstep = _midpoint_distance(q, 7, -126)
+    b = np.where((qdist > 0) & (qdist < _rotation_error(q)), qstep, 0.0)
+    c = float(np.float32(scale * math.log2(math.e)))
+    y = np.abs(x) * c
+    eq = np.array([F8.pow2_exponent(r) for r in y.max(axis=1) * (1.0 + 2.0 ** -7)], dtype=np.float64)
+    _, ex = np.frexp(np.maximum(y, 2.0 ** -300))          # |y| in [2^(ex-1), 2^ex)
+    half = np.maximum(np.ldexp(1.0, ex - 5), np.exp2(eq - 10)[:, None])
+    h = half / c + 2.0 ** -23 * np.abs(x)
+    return a, b, h
 
 
-def fp8_attention_tolerance(q8, k8, v8, scale, weight_eps=2.0 ** -4, out_rel=0.0, flips=None):
+def _query_term(pn, k8, v8, o, scale, query, block=8):
+    """Output shift from the query differences of ``query_shift``: a score
+    s_j = scale q . k_j moves by scale sum_d dq_d k_jd for every key j of
+    the row, so to first order O moves by scale sum_d dq_d Cov_P(k_d, V),
+    Cov_P the covariance of key dim d and the values under the weights P.
+    The known part a enters with its sign, the possible bf16 flips b at
+    worst, and the kernel's rounding r as independent uniform errors (six
+    standard deviations, variance h^2 / 3 each); the sum is taken 1.25
+    times for the second order.  The covariance is formed per row from
+    keys centred on their weighted mean, in fp32 (it only sizes a bound)."""
+    a, b, h = query
+    nq, d = a.shape
+    out = np.zeros_like(o)
+    k32 = k8.astype(np.float32)
+    v32 = v8.astype(np.float32)
+    for i0 in range(0, nq, block):
+        p = pn[i0:i0 + block].astype(np.float32)                 # [B, Nk]
+        m = p @ k32                                              # E_P[k]: [B, d]
+        pk = p[:, :, None] * (k32[None, :, :] - m[:, None, :])   # [B, Nk, d]
+        cov = np.matmul(pk.transpose(0, 2, 1), v32).astype(np.float64)   # [B, d, d]
+        sl = slice(i0, i0 + block)
+        mean = np.abs(np.einsum("bd,bde->be", a[sl], cov))
+        flip = np.einsum("bd,bde->be", b[sl], np.abs(cov))
+        var = np.einsum("bd,bde->be", h[sl] ** 2 / 3.0, cov * cov)
+        out[sl] = 1.25 * scale * (mean + flip + 6.0 * np.sqrt(var))
+    return out
+
+
+def fp8_attention_tolerance(q8, k8, v8, scale, weight_eps=2.0 ** -4, out_rel=0.0, dk=None,
+                            query=None):
     """Per-element bound on |O_gpu - O_oracle| over FP8 pages ([Nq, d] each).
 
     The oracle attends exactly over the dequantised Q, K and V.  The kernel
@@ -119,16 +168,15 @@ def fp8_attention_tolerance(q8, k8, v8, scale, weight_eps=2.0 ** -4, out_rel=0.0
     weight_eps / sqrt 3), six standard deviations of that sum (its
     denominator bounded below by (1 - weight_eps) sum_k P_k), plus out_rel
     |O| for the rounding of the output (bf16: 2^-8), plus 1e-3 for fp32
-    accumulation.  ``flips`` = (dk, dq) from ``key_flips`` (per page, in
-    context order) and ``query_flips``: codes that the kernel's fp32
-    rotation may decide one step away from the oracle's.
-      * A key element off by dk_kd moves score k of row i by at most
-        f_ik = scale sum_d |q8_id| dk_kd, so weight k moves by at most a
-        factor exp(f_ik) and O by at most sum_k w_k |V_k - O| / (1 - sum_k w_k)
-        with w_k = P_k (exp(f_ik) - 1) (|V_k - O| <= |V_k| + |O|).
-      * A query element off by dq_id moves every score of row i by
-        scale dq_id k_kd, one sign for all keys: to first order O moves by
-        scale dq_id Cov_P(k_d, V), taken 1.25 times for the second order.
+    accumulation.
+      * ``dk`` (``key_flips`` of each page, in context order): key codes
+        the kernel's fp32 rotation may decide one step away from the
+        oracle's.  A key element off by dk_kd moves score k of row i by at
+        most f_ik = scale sum_d |q8_id| dk_kd, so weight k moves by at most
+        a factor exp(f_ik) and O by at most sum_k w_k |V_k - O| / (1 - sum_k
+        w_k) with w_k = P_k (exp(f_ik) - 1) (|V_k - O| <= |V_k| + |O|).
+      * ``query`` = ``query_shift(...)``: the kernel quantises the query on
+        another grid than the oracle (``_query_term``).
     """
     s = scale * (q8 @ k8.T)
     s -= s.max(axis=1, keepdims=True)
@@ -140,16 +188,13 @@ def fp8_attention_tolerance(q8, k8, v8, scale, weight_eps=2.0 ** -4, out_rel=0.0
     var = p2 @ (v8 * v8) - 2.0 * o * (p2 @ v8) + o * o * p2.sum(axis=1, keepdims=True)
     spread = np.sqrt(np.maximum(var, 0.0)) / (ps * (1.0 - weight_eps))
     tol = 6.0 * weight_eps / math.sqrt(3.0) * spread + out_rel * np.abs(o) + 1e-3
-    if flips is not None:
-        dk, dq = flips
-        pn = p / ps
+    pn = p / ps
+    if dk is not None:
         w = pn * np.expm1(scale * (np.abs(q8) @ dk.T))
         ws = w.sum(axis=1, keepdims=True)
         tol = tol + (w @ np.abs(v8) + ws * np.abs(o)) / np.maximum(1.0 - ws, 0.5)
-        for i in np.nonzero(dq.any(axis=1))[0]:
-            pk = k8 * pn[i][:, None]
-            cov = pk.T @ v8 - np.outer(pk.sum(axis=0), o[i])      # Cov_P(k_d, V_e)
-            tol[i] += 1.25 * scale * (dq[i] @ np.abs(cov))
+    if query is not None:
+        tol = tol + _query_term(pn, k8, v8, o, scale, query)
     return tol
 
 
@@ -446,11 +491,12 @@ def check_attention(ro, k, layer, rows=None, heads=None, stages=None, seed=0, de
             # exceeds the 1e-3 floor)
             eps, out_rel = (2.0 ** -4 if fp8 is True else 2.0 ** -8), 2.0 ** -8
             tol = np.empty_like(err)
+            sc = WR.scale_of(oc)
             for hi, h in enumerate(hs):
-                q8 = F8.fp8_query(F8.bf16_round(qr[:, h, :]), WR.scale_of(oc))
-                flips = (dk[:, hi, :], query_flips(qr[:, h, :], q8, WR.scale_of(oc)))
-                tol[:, hi, :] = fp8_attention_tolerance(q8, kk[:, hi, :], vv[:, hi, :],
-                                                        WR.scale_of(oc), eps, out_rel, flips)
+                q8 = F8.fp8_query(F8.bf16_round(qr[:, h, :]))
+                tol[:, hi, :] = fp8_attention_tolerance(q8, kk[:, hi, :], vv[:, hi, :], sc, eps,
+                                                        out_rel, dk=dk[:, hi, :],
+                                                        query=query_shift(qr[:, h, :], sc))
             ratio = (err / tol).max()
             worst = max(worst, err.max())
             ro.fp8_bound_ratio = max(getattr(ro, "fp8_bound_ratio", 0.0), ratio)
