@@ -130,6 +130,16 @@ size_t table_bytes(const Shape& sh) {
   return (rope_table_bytes(sh) + 255) / 256 * 256 + split_scratch_bytes(sh);
 }
 
+size_t page_vt_offset(const Shape& sh) {
+  if (sh.dtype == WF_FP8 || sh.dtype == WF_FP8K) return size_t(sh.H) * sh.Npad * sh.D;
+  return size_t(sh.H) * sh.N * sh.D * sh.elem;
+}
+int64_t page_codes_offset(const Shape& sh) {
+  if (sh.dtype == WF_FP8) return int64_t(2) * sh.H * sh.Npad * sh.D;
+  if (sh.dtype == WF_FP8K) return int64_t(3) * sh.H * sh.Npad * sh.D;
+  return -1;
+}
+
 void build_plan(const Shape& sh, uint64_t hash, int64_t k, wf_plan* p) {
   std::memset(p, 0, sizeof(*p));
   p->k = k;

@@ -68,5 +68,8 @@ size_t anchor_bytes(const Shape& sh);
 size_t rope_table_bytes(const Shape& sh);
 size_t split_scratch_bytes(const Shape& sh);
 size_t table_bytes(const Shape& sh);
+// Byte offsets inside one pool page: Vt after K, then (FP8 / FP8K) the codes.
+size_t page_vt_offset(const Shape& sh);
+int64_t page_codes_offset(const Shape& sh);   // -1 when the page has none
 
 }  // namespace wf

@@ -350,6 +350,30 @@ wf_status wf_pool_bytes(const wf_config* cfg, size_t* pool, size_t* anchor, size
   return ok();
 }
 
+wf_status wf_page_layout(const wf_config* cfg, wf_layout* out) {
+  if (!out) return fail(WF_EINVAL, "out is NULL");
+  wf::Shape sh;
+  std::string why;
+  if (!wf::derive_shape(cfg, &sh, &why)) return fail(WF_EINVAL, why);
+  wf_layout l{};
+  l.n_slots = sh.n_slots;
+  l.page_bytes = int64_t(sh.page_bytes);
+  l.pool_bytes = int64_t(wf::pool_bytes(sh));
+  l.anchor_page_bytes = int64_t(sh.anchor_page_bytes);
+  l.anchor_bytes = int64_t(wf::anchor_bytes(sh));
+  l.tokens = sh.N;
+  const bool fp8 = sh.dtype == WF_FP8 || sh.dtype == WF_FP8K;
+  l.tokens_padded = fp8 ? sh.Npad : sh.N;
+  l.tiles = sh.T;
+  l.vt_offset = int64_t(wf::page_vt_offset(sh));
+  l.codes_offset = wf::page_codes_offset(sh);
+  l.table_bytes = int64_t(wf::table_bytes(sh));
+  l.split_scratch_offset = int64_t((wf::rope_table_bytes(sh) + 255) / 256 * 256);
+  l.split_scratch_bytes = int64_t(wf::split_scratch_bytes(sh));
+  *out = l;
+  return ok();
+}
+
 wf_status wf_bind(wf_handle* h, void* d_pool, size_t pool_bytes, void* d_anchor_raw,
                   size_t anchor_bytes, void* d_tables, size_t table_bytes) {
   if (!h) return fail(WF_EINVAL, "handle is NULL");

@@ -28,10 +28,12 @@ class Session:
                    self.tables, self.table_bytes)
         S, N, H, D, L = cfg.S, cfg.F * cfg.Hh * cfg.Ww, cfg.n_heads, cfg.head_dim, cfg.n_layers
         self.S, self.N, self.H, self.D, self.L = S, N, H, D, L
-        self.n_slots = 4 + max(cfg.W, cfg.W + S if cfg.W_store < 0 else cfg.W_store) + 2 * S
-        self.page_bytes = self.pool_bytes // (L * self.n_slots)
-        self.T = (N + 63) // 64
-        self.Npad = 64 * self.T
+        lay = wf.wf_page_layout(cfg)
+        self.layout = lay
+        self.n_slots = lay.n_slots
+        self.page_bytes = lay.page_bytes
+        self.T = lay.tiles
+        self.Npad = lay.tokens_padded
         self.bufs = self.alloc_io() if io else None
 
     def alloc_io(self):
@@ -40,25 +42,26 @@ class Session:
                 for n in ("q", "k", "v", "q_rot", "out")}
 
     # ---- views of the slot pool (layouts documented in include/wf.h) ----
+    def _slot_bytes(self, layer: int, slot: int):
+        return self.pool.view(self.L, self.n_slots, self.page_bytes)[layer, slot]
+
     def page(self, layer: int, slot: int):
         """(K [H][N][D], Vt [H][D][N]) views of one slot of one layer."""
-        hnd = self.H * self.N * self.D
-        pool = self.pool.view(self.dtype).view(self.L, self.n_slots, 2 * hnd)
-        p = pool[layer, slot]
-        return p[:hnd].view(self.H, self.N, self.D), p[hnd:].view(self.H, self.D, self.N)
+        p = self._slot_bytes(layer, slot)
+        vo = self.layout.vt_offset
+        return (p[:vo].view(self.dtype).view(self.H, self.N, self.D),
+                p[vo:2 * vo].view(self.dtype).view(self.H, self.D, self.N))
 
     def fp8_page(self, layer: int, slot: int):
         """(K8 [H][Npad][D], Vt [H][D][Npad], codes [H][T][2]) views of one
         slot of an FP8 or FP8K pool (codes: exponent + 127 of K, V per tile).
         K8 and codes are uint8; Vt is uint8 E4M3 codes (FP8) or bf16 (FP8K)."""
         H, D, Np, T = self.H, self.D, self.Npad, self.T
-        p = self.pool.view(self.L, self.n_slots, self.page_bytes)[layer, slot]
-        kv = H * Np * D
-        vb = 2 * kv if self.cfg.dtype == wf.WF_FP8K else kv
-        vt = p[kv:kv + vb]
+        p = self._slot_bytes(layer, slot)
+        vo, co = self.layout.vt_offset, self.layout.codes_offset
+        vt = p[vo:co]
         vt = vt.view(torch.bfloat16) if self.cfg.dtype == wf.WF_FP8K else vt
-        return (p[:kv].view(H, Np, D), vt.view(H, D, Np),
-                p[kv + vb:kv + vb + 2 * H * T].view(H, T, 2))
+        return p[:vo].view(H, Np, D), vt.view(H, D, Np), p[co:co + 2 * H * T].view(H, T, 2)
 
     def anchor_page(self, layer: int):
         hnd = self.H * self.N * self.D

@@ -51,6 +51,13 @@ class wf_plan(ctypes.Structure):
                 ("kv_tokens", i64), ("flops", f64), ("publish_bytes", f64)]
 
 
+class wf_layout(ctypes.Structure):
+    _fields_ = [(n, i64) for n in
+                ("n_slots", "page_bytes", "pool_bytes", "anchor_page_bytes", "anchor_bytes",
+                 "tokens", "tokens_padded", "tiles", "vt_offset", "codes_offset", "table_bytes",
+                 "split_scratch_offset", "split_scratch_bytes")]
+
+
 class wf_dit_config(ctypes.Structure):
     _fields_ = [("ffn_dim", i32), ("reserved", i32), ("eps", f64)]
 
@@ -84,6 +91,7 @@ def _load():
         "wf_destroy": (None, [H]),
         "wf_pool_bytes": (i32, [ctypes.POINTER(wf_config), ctypes.POINTER(sz),
                                 ctypes.POINTER(sz), ctypes.POINTER(sz)]),
+        "wf_page_layout": (i32, [ctypes.POINTER(wf_config), ctypes.POINTER(wf_layout)]),
         "wf_bind": (i32, [H, vp, sz, vp, sz, vp, sz]),
         "wf_round_plan": (i32, [H, i64, ctypes.POINTER(wf_plan)]),
         "wf_next_round": (i32, [H, ctypes.POINTER(i64)]),
@@ -166,6 +174,12 @@ def wf_pool_bytes(cfg):
     p, a, t = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
     _check(_lib.wf_pool_bytes(ctypes.byref(cfg), ctypes.byref(p), ctypes.byref(a), ctypes.byref(t)))
     return p.value, a.value, t.value
+
+
+def wf_page_layout(cfg):
+    out = wf_layout()
+    _check(_lib.wf_page_layout(ctypes.byref(cfg), ctypes.byref(out)))
+    return out
 
 
 def wf_bind(h, pool, pool_bytes, anchor_raw, anchor_bytes, tables, table_bytes):

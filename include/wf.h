@@ -197,6 +197,27 @@ typedef struct {
   double publish_bytes;            /* publish HBM bytes, all layers          */
 } wf_plan;
 
+/* Where a config's data lives in the caller's buffers (sizes in bytes).
+ * The slot ring (WF App. B.2 Eq. 13: fixed, double-buffered attention slots)
+ * and the page formats are the library's; callers that look inside pages
+ * (tests, debuggers) read the numbers here instead of re-deriving them. */
+typedef struct {
+  int64_t n_slots;               /* pool slots per layer                     */
+  int64_t page_bytes;            /* one slot of one layer                    */
+  int64_t pool_bytes;            /* n_layers * n_slots * page_bytes          */
+  int64_t anchor_page_bytes;     /* one layer's raw anchor K and Vt          */
+  int64_t anchor_bytes;          /* n_layers * anchor_page_bytes             */
+  int64_t tokens;                /* N = F * Hh * Ww                          */
+  int64_t tokens_padded;         /* token rows per page head: 64 * tiles on
+                                    FP8 / FP8K pages, N otherwise           */
+  int64_t tiles;                 /* ceil(N / 64): scale-code tiles per head  */
+  int64_t vt_offset;             /* Vt inside a page (K starts at 0)         */
+  int64_t codes_offset;          /* scale codes inside a page, -1 if none    */
+  int64_t table_bytes;           /* RoPE tables + split scratch              */
+  int64_t split_scratch_offset;  /* split scratch inside the table buffer    */
+  int64_t split_scratch_bytes;   /* 0 for fp32 configs (they never split)    */
+} wf_layout;
+
 typedef struct wf_handle wf_handle;
 
 /* Text for a status code (static storage). */
@@ -217,6 +238,10 @@ void wf_destroy(wf_handle* h);
  * split scratch, see "tables" above).  Any output pointer may be NULL. */
 wf_status wf_pool_bytes(const wf_config* cfg, size_t* pool_bytes,
                         size_t* anchor_bytes, size_t* table_bytes);
+
+/* The layout of `cfg`'s buffers and pages (host only, no device calls).
+ * WF_EINVAL for an invalid config or a NULL pointer. */
+wf_status wf_page_layout(const wf_config* cfg, wf_layout* out);
 
 /* Attach caller-owned device buffers and upload the RoPE tables (computed
  * on the host in fp64, stored as fp32) with a synchronous copy.  Sizes are
@@ -259,7 +284,14 @@ wf_status wf_kv_publish(wf_handle* h, const wf_plan* plan, int32_t layer,
  * groups, followed by one merge launch when groups are split (see
  * wf_set_attention_split).  d_q_rot: [S+1][N][H][D] from wf_kv_publish;
  * d_out: [S+1][N][H][D].
- * WF_EORDER if this layer was not published in this round. */
+ * WF_EORDER if this layer was not published in this round.
+ * Stream order: every attention call of a handle (of any layer and round,
+ * and wf_dit_layer's, which calls this) uses the one split scratch of the
+ * handle's table buffer unless the handle's split mode is WF_SPLIT_OFF or
+ * its dtype is WF_F32.  Such calls must therefore run one after another on
+ * the device: enqueue them on one stream, or order them with events.  Two
+ * of them in flight at once on different streams overwrite each other's
+ * partial results.  Publishes need no such order among themselves. */
 wf_status wf_wave_attention(wf_handle* h, const wf_plan* plan, int32_t layer,
                             const void* d_q_rot, void* d_out, void* stream);
 

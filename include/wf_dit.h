@@ -81,8 +81,11 @@ wf_status wf_dit_workspace_bytes(const wf_handle* h, const wf_dit_config* dc, si
 /* Layer `layer` of the round's DiT forward for every active cell, in place
  * on x (the block above).  Runs this layer's wf_kv_publish and
  * wf_wave_attention internally, so the same ordering rules apply: the plan
- * must be the handle's next round (WF_EORDER), and wf_round_commit ends the
- * round after every layer has run.  `mod` is this layer's [S+1][6][C].
+ * must be the handle's next round (WF_EORDER), wf_round_commit ends the
+ * round after every layer has run, and calls on one handle must run one
+ * after another on the device (one stream, or ordered by events), because
+ * their attention shares the handle's split scratch and their products the
+ * one work buffer.  `mod` is this layer's [S+1][6][C].
  * Everything is enqueued on `stream`.  WF_ESMALL if work_bytes is below
  * wf_dit_workspace_bytes; WF_EINVAL for NULL or misaligned (16-byte)
  * pointers; WF_EDEVICE if a launch or a hipBLASLt call fails. */

@@ -32,7 +32,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     assert {"wf_dit_workspace_bytes", "wf_dit_layer", "wf_dit_round"} <= set(names)
     lib = ctypes.CDLL(wf.LIB_PATH)
     for n in names:
@@ -89,6 +89,39 @@ def test_pool_bytes():
     # RoPE tables rounded up to 256 bytes, then the split scratch: two split
     # groups x two halves x (O [N][H][D] + (e, l) [N][H]) in fp32
     assert tab == -(-rope // 256) * 256 + 2 * 2 * (nh * 128 + 2 * nh) * 4
+
+
+@pytest.mark.parametrize("w", list(ALL.values()), ids=lambda w: w.name)
+def test_page_layout_matches_the_page_formats(w):
+    """wf_page_layout: the slot count is the oracle's ring (4 + max(W,
+    W_store) + 2 S), the sizes agree with wf_pool_bytes, and the offsets are
+    those of the page formats in wf.h (K at 0; Vt after H x Npad x D keys of
+    1 byte on FP8 / FP8K pages, else H x N x D elements; codes after Vt)."""
+    cfg = w.config()
+    lay = wf.wf_page_layout(cfg)
+    pool, anc, tab = wf.wf_pool_bytes(cfg)
+    oc = oracle_cfg(cfg)
+    N, H, D, L = w.n_tokens, w.n_heads, w.head_dim, w.n_layers
+    T = -(-N // 64)
+    assert lay.n_slots == oc.n_slots
+    assert (lay.pool_bytes, lay.anchor_bytes, lay.table_bytes) == (pool, anc, tab)
+    assert lay.pool_bytes == L * lay.n_slots * lay.page_bytes
+    assert lay.anchor_bytes == L * lay.anchor_page_bytes == L * 2 * H * N * D * (4 if w.dtype == wf.WF_F32 else 2)
+    assert (lay.tokens, lay.tiles) == (N, T)
+    if w.dtype in (wf.WF_FP8, wf.WF_FP8K):
+        vb = 1 if w.dtype == wf.WF_FP8 else 2
+        assert lay.tokens_padded == 64 * T
+        assert lay.vt_offset == H * 64 * T * D
+        assert lay.codes_offset == lay.vt_offset + vb * H * 64 * T * D
+        assert lay.page_bytes == -(-(lay.codes_offset + 2 * H * T) // 256) * 256
+    else:
+        eb = 4 if w.dtype == wf.WF_F32 else 2
+        assert lay.tokens_padded == N and lay.codes_offset == -1
+        assert lay.vt_offset == H * N * D * eb and lay.page_bytes == 2 * lay.vt_offset
+    nh = N * H
+    assert lay.split_scratch_bytes == (0 if w.dtype == wf.WF_F32 else 2 * 2 * (nh * D + 2 * nh) * 4)
+    assert lay.split_scratch_offset % 256 == 0
+    assert lay.split_scratch_offset + lay.split_scratch_bytes == lay.table_bytes
 
 
 def test_pool_bytes_fp8():

@@ -4,7 +4,9 @@
   active chunk (stage j < s) leaves every stage-s output bit-identical.
 * Same-graph scheduling (WF App. B.6, Proposition 1): the order and the
   streams the per-layer work is issued on do not change a single bit, as
-  long as every attention runs after its layer's publish.
+  long as every attention runs after its layer's publish and the attention
+  calls of a handle run one after another (they share the handle's split
+  scratch; include/wf.h states the rule).
 * Stale slots: slots a round neither reads nor writes may hold anything
   (NaN here) without touching the outputs.
 * HIP graphs: a round's layers captured into a graph replay to the eager bits.
