@@ -177,12 +177,16 @@ def test_full_size_wan13b_4step_sampled():
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("w", [WAN13B_5STEP, WAN13B_5STEP_ROLLING], ids=lambda w: w.name)
 def test_full_size_wan13b_5step_sampled(w):
+    """1.3B shape, 5 steps (and the Rolling-Forcing mask): the first steady
+    round with the anchor re-rotated (k=17), first and last layer, whole
+    pages and q_rot, 64 sampled rows per (group, head) plus the last row."""
     ro = Rollout(w)
     try:
         for k in range(18):
             _log(f"{w.name} round {k}")
             ro.run(k)
         for layer in (0, w.n_layers - 1):
+            check_publish(ro, 17, layer)
             err = check_attention(ro, 17, layer, rows=64)
             _log(f"  k=17 layer={layer} max abs err {err:.3e}")
     finally:
@@ -191,14 +195,46 @@ def test_full_size_wan13b_5step_sampled(w):
 
 @pytest.mark.timeout(1200)
 def test_full_size_wan14b_4step_sampled():
+    """14B-class shape (40 heads, per-head query scale U(0.5, 2)): two
+    steady rounds (14: the anchor's first shift; 15), first and last layer,
+    64 sampled rows per (group, head) plus the last row, at the fixed 2e-2
+    bar; whole pages of the first layer."""
     w = WAN14B_4STEP
     ro = Rollout(w)
     try:
-        for k in range(15):
+        for k in range(16):
             _log(f"{w.name} round {k}")
             ro.run(k)
-        err = check_attention(ro, 14, w.n_layers - 1, rows=32)
-        _log(f"  k=14 layer={w.n_layers - 1} max abs err {err:.3e}")
+            if k in (14, 15):
+                for layer in (0, w.n_layers - 1):
+                    if layer == 0:
+                        check_publish(ro, k, layer)
+                    err = check_attention(ro, k, layer, rows=64)
+                    _log(f"  k={k} layer={layer} max abs err {err:.3e}")
+    finally:
+        ro.close()
+
+
+@pytest.mark.timeout(1200)
+def test_full_size_wan13b_long_rollout_two_layers():
+    """The 133-chunk request at the 1.3B shape (137 rounds, automatic split)
+    with two layers (layers are independent, so two bound the time): the
+    slot ring wraps many times (k = 24, 70, 132) and the drain rounds
+    133-136 run partial widths, where the split picks other groups.  Whole
+    pages, q_rot and 32 sampled rows per (group, head) plus the last row,
+    both layers."""
+    w = WAN13B_4STEP.with_(name="wan1.3b_4step_2layer_rollout", n_layers=2)
+    checked = (24, 70, 132, 133, 134, 135, 136)
+    ro = Rollout(w)
+    try:
+        for k in range(w.n_chunk + w.S):
+            ro.run(k)
+            if k in checked:
+                _log(f"{w.name} round {k}")
+                for layer in range(w.n_layers):
+                    check_publish(ro, k, layer)
+                    err = check_attention(ro, k, layer, rows=32)
+                    _log(f"  k={k} layer={layer} max abs err {err:.3e}")
     finally:
         ro.close()
 
