@@ -41,6 +41,11 @@ reason in the design notes):
 * Rolling-Forcing comparison mask: every active denoising chunk reads every
   active denoising chunk, ordered by increasing stage; the store is unchanged.
 * Inactive cells (fill/drain) contribute no keys at all.
+* Unbounded requests (``n_chunk <= 0``): WF §1 and App. B.8 describe a
+  continuous stream whose attention storage does not grow with its length.
+  Such a request has no last chunk, so every chunk i >= 0 exists: after the
+  fill every round is full width and there is no drain.  Its plan of round k
+  equals the plan of any bounded request with more than k chunks.
 """
 
 from dataclasses import dataclass
@@ -90,13 +95,19 @@ class Config:
         return 4 + self.w_max + 2 * self.S
 
     @property
+    def unbounded(self) -> bool:
+        return self.n_chunk <= 0
+
+    @property
     def n_rounds(self) -> int:
         """WF App. B.3: N_chunk + S rounds including fill and drain."""
+        if self.unbounded:
+            raise ValueError("an unbounded request has no last round")
         return self.n_chunk + self.S
 
 
 def chunk_active(cfg: Config, i: int) -> bool:
-    return 0 <= i < cfg.n_chunk
+    return i >= 0 and (cfg.unbounded or i < cfg.n_chunk)
 
 
 def denoise_active(cfg: Config, k: int):
@@ -186,7 +197,7 @@ def evicted_chunk(cfg: Config, k: int) -> int:
 
 def plan(cfg: Config, k: int) -> dict:
     """The full plan of round k as plain Python data."""
-    if not (0 <= k < cfg.n_rounds):
+    if k < 0 or (not cfg.unbounded and k >= cfg.n_rounds):
         raise ValueError("round out of range")
     cells = []
     for s in range(cfg.S + 1):

@@ -196,10 +196,38 @@ def test_slot_ring_brute_force(c):
     every key entry it reads must find the identity it names, written in this
     round or promoted earlier and not overwritten since.  Round k+1 must not
     write any slot that round k reads (double buffering of Eq. 13)."""
+    _simulate_slots(c, c.n_rounds)
+
+
+@pytest.mark.parametrize("c", [cfg(S=4, W=4, n_chunk=0), cfg(S=2, W=2, W_store=4, n_chunk=-1),
+                               cfg(S=3, W=0, anchor=0, n_chunk=0),
+                               cfg(S=5, W=6, n_chunk=0, mask=P.MASK_ROLLING)],
+                         ids=lambda c: f"S{c.S}W{c.W}/{c.W_store}A{c.anchor}m{c.mask}")
+def test_unbounded_request(c):
+    """An unbounded request: every round from S on is full width with one
+    store, slots stay within the same n_slots over 400 rounds (the ring keeps
+    attention storage bounded, App. B.8), and round k's plan equals the plan
+    of a bounded request of k + 1 + S chunks (so a stream can be ended at any
+    round and drain like a bounded one)."""
+    rounds = 400
+    _simulate_slots(c, rounds)
+    for k in range(rounds):
+        p = P.plan(c, k)
+        assert p["n_active"] == min(k + 1, c.S + 1)
+        assert p["cells"][c.S]["active"] == (k >= c.S)
+        if k % 37 == 0 or k < 3 * c.S:
+            b = P.Config(**{**c.__dict__, "n_chunk": k + 1 + c.S})
+            assert P.plan(b, k) == p
+    with pytest.raises(ValueError):
+        c.n_rounds
+
+
+def _simulate_slots(c, rounds):
+    plans = [P.plan(c, k) for k in range(rounds)]
     content = {}
     prev_reads = set()
-    for k in range(c.n_rounds):
-        p = P.plan(c, k)
+    for k in range(rounds):
+        p = plans[k]
         writes = {}
         for x in p["cells"]:
             if x["active"]:
@@ -226,8 +254,8 @@ def test_slot_ring_brute_force(c):
         # evicted chunk is no longer read in any later round
         ev = p["evict"]
         if ev >= 0:
-            for k2 in range(k + 1, c.n_rounds):
-                for g in P.plan(c, k2)["groups"]:
+            for k2 in range(k + 1, rounds):
+                for g in plans[k2]["groups"]:
                     assert all(not (kd == P.HISTORY and ch == ev)
                                for kd, ch, _ in g["entries"])
         prev_reads = reads

@@ -179,9 +179,9 @@ def fp8_attention_tolerance(q8, k8, v8, scale, weight_eps=2.0 ** -4, out_rel=0.0
       * ``query`` = ``query_shift(...)``: the kernel quantises the query on
         another grid than the oracle (``_query_term``).  Given ``err`` (the
         observed |O_gpu - O_oracle|), the term is formed only for the rows
-        where some element exceeds the other terms: the others pass either
-        way, and their returned bound (without the term) is smaller than the
-        full one, so err / bound never understates.
+        where some element exceeds half the other terms: the others pass
+        either way, and their err / bound, at most 0.5 without the term,
+        never understates; above 0.5 the returned bound is the full one.
     """
     s = scale * (q8 @ k8.T)
     s -= s.max(axis=1, keepdims=True)
@@ -199,7 +199,7 @@ def fp8_attention_tolerance(q8, k8, v8, scale, weight_eps=2.0 ** -4, out_rel=0.0
         ws = w.sum(axis=1, keepdims=True)
         tol = tol + (w @ np.abs(v8) + ws * np.abs(o)) / np.maximum(1.0 - ws, 0.5)
     if query is not None:
-        rows = np.arange(q8.shape[0]) if err is None else np.nonzero((err > tol).any(axis=1))[0]
+        rows = np.arange(q8.shape[0]) if err is None else np.nonzero((err > 0.5 * tol).any(axis=1))[0]
         if len(rows):
             sub = tuple(x[rows] for x in query)
             tol[rows] += _query_term(pn[rows], k8, v8, o[rows], scale, sub)
