@@ -49,8 +49,11 @@ wf_status check_plan(const wf_handle* h, const wf_plan* p, wf_plan* fresh);
 wf_status check_layer_call(const wf_handle* h, int32_t layer);
 wf_status do_publish(wf_handle* h, const wf_plan& p, int layer, const void* q, const void* k,
                      const void* v, void* q_rot, hipStream_t stream);
+// Split groups leave their partial results in `scratch` (capacity
+// `scratch_cap` bytes), by default the split scratch of the handle's table
+// buffer; WF_ESMALL before any launch when the split chosen needs more.
 wf_status do_attention(wf_handle* h, const wf_plan& p, int layer, const void* q_rot, void* out,
-                       hipStream_t stream);
+                       hipStream_t stream, char* scratch = nullptr, size_t scratch_cap = 0);
 
 }  // namespace rt
 }  // namespace wf

@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstring>
 #include <functional>
+#include <mutex>
 #include <queue>
 #include <string>
 #include <vector>
@@ -209,7 +210,7 @@ std::vector<int> choose_split(wf_handle* h, const wf_plan& p, const std::vector<
 }
 
 wf_status do_attention(wf_handle* h, const wf_plan& p, int layer, const void* q_rot, void* out,
-                       hipStream_t stream) {
+                       hipStream_t stream, char* scratch, size_t scratch_cap) {
   const wf::Shape& sh = h->sh;
   wf::AttnArgs a{};
   a.q_rot = q_rot;
@@ -268,10 +269,23 @@ wf_status do_attention(wf_handle* h, const wf_plan& p, int layer, const void* q_
   }
   a.n_groups = static_cast<int>(runs.size());
   a.n_items = item;
-  char* scratch = static_cast<char*>(h->tables) + (wf::rope_table_bytes(sh) + 255) / 256 * 256;
-  const size_t nhd = size_t(sh.N) * size_t(sh.H) * size_t(sh.D);
+  if (!scratch) {
+    scratch = static_cast<char*>(h->tables) + (wf::rope_table_bytes(sh) + 255) / 256 * 256;
+    scratch_cap = wf::split_scratch_bytes(sh);
+  }
+  // Two halves per split group: O [N][H][D] fp32 of every half, then (e, l)
+  // [N][H] of every half.
+  const size_t nh = size_t(sh.N) * size_t(sh.H);
+  const size_t nhd = nh * size_t(sh.D);
+  const size_t parts = 2 * split.size();
+  const size_t need = parts * (nhd + 2 * nh) * sizeof(float);
+  if (need > scratch_cap) {
+    return fail(WF_ESMALL, "the split chosen needs " + std::to_string(need) +
+                               " bytes of split scratch, above the " + std::to_string(scratch_cap) +
+                               " available (WF_SPLIT_OFF needs none)");
+  }
   a.part_o = reinterpret_cast<float*>(scratch);
-  a.part_el = reinterpret_cast<float*>(scratch + size_t(wf::kMaxSplit) * 2 * nhd * sizeof(float));
+  a.part_el = reinterpret_cast<float*>(scratch + parts * nhd * sizeof(float));
   (void)hipGetLastError();
   hipError_t e = sh.dtype == WF_FP8    ? wf::launch_attention_fp8(a, stream)
                  : sh.dtype == WF_FP8K ? wf::launch_attention_fp8k(a, stream)
@@ -288,6 +302,35 @@ wf_status do_attention(wf_handle* h, const wf_plan& p, int layer, const void* q_
     e = wf::launch_combine(c, stream);
     if (e != hipSuccess) return fail(WF_EDEVICE, std::string("combine launch: ") + hipGetErrorString(e));
   }
+  return ok();
+}
+
+// ---- split scratch of the allocation-free attention entry point ----
+// One file-scope device array, which every GPU the library runs on holds
+// until the process ends.  Host code never names it directly: the array's
+// host-side name is no device address.  Its address on each device is
+// looked up once, with that device current, and kept here.
+constexpr size_t kStaticScratchBytes = size_t(WF_STATIC_SCRATCH_BYTES);
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+wf_status static_scratch(char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(WF_EDEVICE, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(WF_EUNSUPPORTED, "device index above 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(WF_EDEVICE, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = static_cast<char*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
   return ok();
 }
 
@@ -469,6 +512,22 @@ wf_status wf_wave_attention(wf_handle* h, const wf_plan* plan, int32_t layer, co
   if (!aligned16(d_q_rot) || !aligned16(d_out))
     return fail(WF_EINVAL, "q_rot and out must be 16-byte aligned");
   return do_attention(h, p, layer, d_q_rot, d_out, static_cast<hipStream_t>(stream));
+}
+
+wf_status wf_wave_attention_noalloc(wf_handle* h, const wf_plan* plan, int32_t layer,
+                                    const void* d_q_rot, void* d_out, void* stream) {
+  wf_plan p;
+  wf_status s = check_plan(h, plan, &p);
+  if (s != WF_OK) return s;
+  if ((s = check_layer_call(h, layer)) != WF_OK) return s;
+  if (!h->published[layer]) return fail(WF_EORDER, "layer not published in this round");
+  if (!d_q_rot || !d_out) return fail(WF_EINVAL, "q_rot or out is NULL");
+  if (!aligned16(d_q_rot) || !aligned16(d_out))
+    return fail(WF_EINVAL, "q_rot and out must be 16-byte aligned");
+  char* base = nullptr;
+  if ((s = static_scratch(&base)) != WF_OK) return s;
+  return do_attention(h, p, layer, d_q_rot, d_out, static_cast<hipStream_t>(stream), base,
+                      kStaticScratchBytes);
 }
 
 wf_status wf_round_commit(wf_handle* h, const wf_plan* plan) {

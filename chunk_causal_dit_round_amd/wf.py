@@ -98,6 +98,7 @@ def _load():
         "wf_reset": (i32, [H]),
         "wf_kv_publish": (i32, [H, ctypes.POINTER(wf_plan), i32, cvp, cvp, cvp, vp, vp]),
         "wf_wave_attention": (i32, [H, ctypes.POINTER(wf_plan), i32, cvp, vp, vp]),
+        "wf_wave_attention_noalloc": (i32, [H, ctypes.POINTER(wf_plan), i32, cvp, vp, vp]),
         "wf_set_attention_split": (i32, [H, i32]),
         "wf_round_commit": (i32, [H, ctypes.POINTER(wf_plan)]),
         "wf_round": (i32, [H, ctypes.POINTER(wf_plan), cvp, cvp, cvp, vp, vp, vp]),
@@ -211,6 +212,14 @@ def wf_kv_publish(h, plan, layer, q, k, v, q_rot, stream=None):
 def wf_wave_attention(h, plan, layer, q_rot, out, stream=None):
     _check(_lib.wf_wave_attention(h, ctypes.byref(plan), layer, _ptr(q_rot), _ptr(out),
                                   _stream(stream)))
+
+
+def wf_wave_attention_noalloc(h, plan, layer, q_rot, out, stream=None):
+    _check(_lib.wf_wave_attention_noalloc(h, ctypes.byref(plan), layer, _ptr(q_rot), _ptr(out),
+                                          _stream(stream)))
+
+
+WF_STATIC_SCRATCH_BYTES = 128 << 20
 
 
 def wf_set_attention_split(h, mode):

@@ -295,6 +295,27 @@ wf_status wf_kv_publish(wf_handle* h, const wf_plan* plan, int32_t layer,
 wf_status wf_wave_attention(wf_handle* h, const wf_plan* plan, int32_t layer,
                             const void* d_q_rot, void* d_out, void* stream);
 
+/* Bytes of the library's static split scratch (wf_wave_attention_noalloc). */
+#define WF_STATIC_SCRATCH_BYTES (128u << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * wf_wave_attention with the split groups' partial results kept in a static
+ * device array of the library (WF_STATIC_SCRATCH_BYTES = 128 MiB, held by
+ * every GPU the library runs on until the process ends) instead of the
+ * handle's table buffer.  Arguments, results, validation and stream-order
+ * rules are those of wf_wave_attention; the call allocates nothing (the
+ * array's device address is looked up once per device, on the first call
+ * with that device current).  Every call on one GPU, from any handle,
+ * shares that GPU's one array and leaves its partial results there, so two
+ * such calls in flight at once on one GPU (different streams, handles or
+ * threads) race: order them.  WF_ESMALL, before any launch, when the split
+ * the handle's mode chooses needs more than WF_STATIC_SCRATCH_BYTES
+ * (2 (N H D + 2 N H) * 4 bytes per split group); WF_SPLIT_OFF needs none.
+ * WF_EDEVICE if the array's address cannot be found. */
+wf_status wf_wave_attention_noalloc(wf_handle* h, const wf_plan* plan, int32_t layer,
+                                    const void* d_q_rot, void* d_out, void* stream);
+
 /* How wf_wave_attention divides its work (bf16, FP8 and FP8K rounds; fp32
  * rounds never split).  A launch runs one work-group per (group, head, 256
  * query rows), each over the group's whole context, so the launch ends with
