@@ -15,6 +15,11 @@ the launch stream around every attention launch in the timed region.
 `cpu_baseline` is the fp64 oracle on a bounded sample, timed on this host.
 
 Other modes (one JSON line each):
+  --workload tiny_fp32_s2
+                     a request shorter than the steady window (the tiny fp32
+                     round: 6 chunks, 8 rounds): a step is the whole request
+                     from round 0 (fill, full width, drain); the fp32 path is
+                     bound by the vector ALUs (157.3 TFLOP/s fp32).
   --rollout          the whole long request (133 chunks, 137 rounds) with fresh
                      per-round inputs (generated between rounds, untimed): steady,
                      full-width and whole-request rounds/s.
@@ -54,6 +59,7 @@ PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 # so its peak is the harmonic blend, 3.33 PFLOP/s.
 PEAK_FP8K_TFLOPS = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
 PEAK_HBM_GBPS = 8000.0
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector (plain FMA on the SIMDs)
 CSRC = os.path.join(ROOT, "chunk_causal_dit_round_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -99,8 +105,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="wan1.3b_4step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=1,
-                    help="heads of one layer the oracle baseline times")
+    ap.add_argument("--cpu-heads", type=int, default=0,
+                    help="heads of one layer the oracle baseline times (0: all, one whole layer)")
     ap.add_argument("--rollout", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--dit", action="store_true")
@@ -185,12 +191,113 @@ def oracle_baseline(w, k, layer, heads, raw, fp8=False):
     frac = len(heads) / (w.n_heads * w.n_layers)   # share of one round
     t_round = dt / frac
     cores = len(os.sched_getaffinity(0))
+    which = ("all heads (one whole layer)" if len(heads) == w.n_heads
+             else f"heads {list(heads)} of {w.n_heads}")
     return {"value": 1.0 / t_round, "unit": "rounds/s", "cores": threads or cores,
             "kind": "oracle",
-            "sample": f"fp64 oracle, round k={k}, layer {layer}, heads {list(heads)} of "
-                      f"{w.n_heads}, every query group over its full context: {dt:.1f} s, "
-                      f"scaled by {1 / frac:.0f} to one round ({w.n_layers} layers x "
-                      f"{w.n_heads} heads); host has {cores} cores"}
+            "sample": f"fp64 oracle, round k={k}, layer {layer}, {which}, every query group "
+                      f"over its full context: {dt:.1f} s, scaled by {1 / frac:.0f} to one round "
+                      f"({w.n_layers} layers x {w.n_heads} heads); host has {cores} cores"}
+
+
+def request_bench(args, w):
+    """A request shorter than the steady window (the tiny fp32 round): a
+    step is the whole request, every round (fill, full width, drain) from
+    round 0, with each round's seeded inputs resident in HBM.  value =
+    rounds/s over the timed requests."""
+    import torch
+
+    from chunk_causal_dit_round_amd import synth, wf
+    from chunk_causal_dit_round_amd.session import Session
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sess = Session(w.config(), device=dev)
+    S, L = w.S, w.n_layers
+    n_rounds = w.n_chunk + w.S
+    sets = []
+    for k in range(n_rounds):
+        b = sess.alloc_io() if k else sess.bufs
+        synth.fill_round(b, "bench", k, L, S + 1)
+        if k:
+            b["q_rot"], b["out"] = sess.bufs["q_rot"], sess.bufs["out"]
+        sets.append(b)
+    plans = [sess.plan(k) for k in range(n_rounds)]
+    stream = torch.cuda.current_stream()
+
+    def request(ev=None):
+        wf.wf_reset(sess.h)
+        for k in range(n_rounds):
+            for layer in range(L):
+                sess.publish(plans[k], layer, sets[k], stream)
+                if ev is not None:
+                    ev[k][layer][0].record(stream)
+                sess.attention(plans[k], layer, sets[k], stream)
+                if ev is not None:
+                    ev[k][layer][1].record(stream)
+            sess.commit(plans[k])
+
+    for _ in range(args.warmup):
+        request()
+    torch.cuda.synchronize()
+    events = [[[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(L)]
+               for _ in range(n_rounds)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        request(events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    att_s = sum(e[k][l][0].elapsed_time(e[k][l][1]) for e in events for k in range(n_rounds)
+                for l in range(L)) / 1e3
+    flops = sum(p.flops for p in plans) * args.steps
+    achieved = flops / att_s / 1e12
+    fp32 = w.dtype == wf.WF_F32
+    # fp32 rounds run plain fp32 FMA on the vector ALUs, whose published peak
+    # is 157.3 TFLOP/s (256 CUs x 2.4 GHz x 256 FLOP per CU per clock)
+    peak = PEAK_FP32_TFLOPS if fp32 else PEAK_BF16_TFLOPS
+    res = {
+        "metric": "wavefront rounds/sec (=chunks/sec) and attention TFLOP/s",
+        "value": args.steps * n_rounds / elapsed, "unit": "rounds/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": 1e3 * elapsed / args.steps, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp32" if fp32 else "bf16", "data": "synthetic",
+        "config": {"workload": f"{w.name} whole request ({w.n_chunk} chunks, {n_rounds} rounds: "
+                               f"fill, full width, drain), a step = the whole request",
+                   "S": w.S, "W": w.W, "tokens_per_chunk": w.n_tokens, "heads": w.n_heads,
+                   "head_dim": w.head_dim, "layers": L, "n_rounds": n_rounds},
+        "roofline": {"bound": "alu" if fp32 else "mfma", "achieved": achieved, "peak": peak,
+                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
+                     "kernel": "wf_attention_f32_kernel" if fp32 else "wf_attention_bf16_kernel",
+                     "flops_per_request": flops / args.steps,
+                     "attention_ms_per_request": 1e3 * att_s / args.steps},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import wf_plan as P
+        from oracle import wf_round as WR
+
+        def raw(rnd, layer, stage, name):
+            x = synth.slice_input("bench", rnd, layer, stage, name, sess.N, sess.H, sess.D, dev,
+                                  sess.dtype)
+            return x.to(torch.float64).cpu().numpy()
+        oc = P.Config(S=w.S, W=w.W, W_store=w.W_store, anchor=w.anchor, n_chunk=w.n_chunk,
+                      F=w.F, Hh=w.Hh, Ww=w.Ww, n_heads=w.n_heads, head_dim=w.head_dim,
+                      n_layers=w.n_layers, mask=w.mask)
+        for k in range(n_rounds):               # inputs regenerated before timing
+            for layer in range(L):
+                for st in range(S + 1):
+                    for name in ("q", "k", "v"):
+                        raw(k, layer, st, name)
+        t0 = time.perf_counter()
+        for k in range(n_rounds):
+            for layer in range(L):
+                WR.round_outputs(oc, k, layer, raw)
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": n_rounds / dt, "unit": "rounds/s",
+                               "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+                               "sample": f"fp64 oracle, the whole request ({n_rounds} rounds, "
+                                         f"every layer, group and head, input generation "
+                                         f"untimed): {dt:.2f} s"}
+    print(json.dumps(res), flush=True)
 
 
 def dit_oracle_baseline(ds, w, k):
@@ -389,6 +496,9 @@ def main():
     w_store = w.W + w.S if w.W_store < 0 else w.W_store
     k_steady = w.S + max(w.W, w_store) + 1         # full width and full window
     n_rounds = w.n_chunk + w.S
+    if w.n_chunk + w.S <= 64:
+        request_bench(args, w)
+        return
     if k_steady + args.warmup + args.steps > w.n_chunk:
         print("steps + warmup exceed the steady rounds of one request", file=sys.stderr)
         sys.exit(2)
@@ -484,7 +594,8 @@ def main():
             x = synth.slice_input("bench", rnd % 2, layer, stage, name, sess.N, sess.H, sess.D,
                                   dev, sess.dtype)
             return x.to(torch.float64).cpu().numpy()
-        res["cpu_baseline"] = oracle_baseline(w, k0, 0, list(range(args.cpu_heads)), raw, fp8=fp8)
+        heads = list(range(args.cpu_heads or w.n_heads))
+        res["cpu_baseline"] = oracle_baseline(w, k0, 0, heads, raw, fp8=fp8)
     print(json.dumps(res), flush=True)
 
 

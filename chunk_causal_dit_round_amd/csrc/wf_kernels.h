@@ -33,11 +33,13 @@ struct PublishArgs {
   void* q_rot;            // this layer's [S+1][N][H][D]
   void* pool;             // this layer's [n_slots] pages
   void* anchor_raw;       // this layer's anchor page (raw K, Vt)
-  const float2* rope;     // [n_frames*nt | Hh*nh | Ww*nw] (cos, sin)
+  const double* omega_t;  // [nt] frame-axis frequencies theta^(-m / nt)
+  const float2* rope_hw;  // [Hh*nh | Ww*nw] (cos, sin) of the row and column axes
   int64_t page_elems;     // 2 H N D (fp32 / bf16 pages)
   int64_t page_bytes;     // bytes per pool page (all dtypes)
   int32_t N, H, D, F, Hh, Ww;
-  int32_t nt, nh, nw, n_frames;
+  int32_t nt, nh, nw;
+  int32_t heads_per_group;  // set by the launcher
   int32_t Npad, T;        // FP8 pages: tokens padded to 64 T, T tiles
   int32_t n_tasks;
   int32_t pad_;
@@ -91,6 +93,11 @@ constexpr int kAttnBM_fp8k = 256;
 constexpr int kAttnBM_f32 = 64;
 // FP8 / FP8K attention keeps the scale codes of a group's whole context in LDS.
 constexpr int kFp8MaxCtxTiles = 4096;
+
+// The publish kernels compute the frame-axis cos/sin of a 64-token block in
+// LDS: at most 64 frames x the frame axis's pairs (22 for head_dim <= 128).
+constexpr int kMaxFramePairs = 22;
+constexpr int kMaxFrameEntries = 64 * kMaxFramePairs;
 
 hipError_t launch_publish(const PublishArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_attention(const AttnArgs& a, int dtype, hipStream_t stream);

@@ -15,7 +15,7 @@ bool fail(std::string* why, const char* msg) {
 }
 
 // Chunk i exists in the request.
-inline bool live(const Shape& sh, int64_t i) { return i >= 0 && i < sh.n_chunk; }
+inline bool live(const Shape& sh, int64_t i) { return i >= 0 && (sh.unbounded || i < sh.n_chunk); }
 
 }  // namespace
 
@@ -26,9 +26,14 @@ bool derive_shape(const wf_config* c, Shape* o, std::string* why) {
   if (c->W_store < -1 || c->W_store > WF_MAX_PAGES)
     return fail(why, "W_store must be -1 or in [0, 48]");
   if (c->anchor != 0 && c->anchor != 1) return fail(why, "anchor must be 0 or 1");
-  if (c->n_chunk < 1 || c->n_chunk > (1 << 20))
-    return fail(why, "n_chunk must be in [1, 2^20]");
   if (c->F < 1 || c->Hh < 1 || c->Ww < 1) return fail(why, "F, Hh, Ww must be >= 1");
+  if (c->n_chunk >= 1) {
+    if (int64_t(c->n_chunk) * c->F > (int64_t(1) << 30))
+      return fail(why, "n_chunk * F must be <= 2^30 (frame positions)");
+    if (c->max_frames != 0) return fail(why, "max_frames must be 0 for a bounded request (n_chunk >= 1)");
+  } else if (c->max_frames < c->F || c->max_frames > (1 << 30)) {
+    return fail(why, "an unbounded request (n_chunk <= 0) needs max_frames in [F, 2^30]");
+  }
   const int64_t n = int64_t(c->F) * c->Hh * c->Ww;
   if (n > (1 << 24)) return fail(why, "tokens per chunk F*Hh*Ww must be <= 2^24");
   if (c->n_heads < 1 || c->n_heads > 1024) return fail(why, "n_heads must be in [1, 1024]");
@@ -39,7 +44,6 @@ bool derive_shape(const wf_config* c, Shape* o, std::string* why) {
     return fail(why, "dtype must be WF_F32, WF_BF16, WF_FP8 or WF_FP8K");
   if (c->mask != WF_MASK_WAVE && c->mask != WF_MASK_ROLLING)
     return fail(why, "mask must be WF_MASK_WAVE or WF_MASK_ROLLING");
-  if (c->reserved != 0) return fail(why, "reserved must be 0");
   if (!(c->rope_theta >= 0.0) || !std::isfinite(c->rope_theta) ||
       (c->rope_theta != 0.0 && c->rope_theta <= 1.0))
     return fail(why, "rope_theta must be 0 (default) or > 1");
@@ -53,7 +57,9 @@ bool derive_shape(const wf_config* c, Shape* o, std::string* why) {
   s.Wmax = s.W > s.Ws ? s.W : s.Ws;
   s.ring = s.Wmax + 2;
   s.anchor = c->anchor;
-  s.n_chunk = c->n_chunk;
+  s.unbounded = c->n_chunk <= 0;
+  s.n_chunk = s.unbounded ? 0 : c->n_chunk;
+  s.max_frames = c->max_frames;
   s.F = c->F;
   s.Hh = c->Hh;
   s.Ww = c->Ww;
@@ -68,7 +74,6 @@ bool derive_shape(const wf_config* c, Shape* o, std::string* why) {
   s.nh = s.D / 6;
   s.nw = s.nh;
   s.nt = s.D / 2 - 2 * s.nh;
-  s.n_frames = s.n_chunk * s.F;
   s.dtype = c->dtype;
   s.mask = c->mask;
   s.theta = c->rope_theta == 0.0 ? 10000.0 : c->rope_theta;
@@ -106,8 +111,8 @@ uint64_t config_hash(const wf_config& c) {
       h *= 1099511628211ull;
     }
   };
-  const int32_t ints[] = {c.S, c.W, c.W_store, c.anchor, c.n_chunk, c.F, c.Hh, c.Ww,
-                          c.n_heads, c.head_dim, c.n_layers, c.dtype, c.mask};
+  const int32_t ints[] = {c.S, c.W, c.W_store, c.anchor, c.n_chunk <= 0 ? 0 : c.n_chunk, c.F, c.Hh, c.Ww,
+                          c.n_heads, c.head_dim, c.n_layers, c.dtype, c.mask, c.max_frames};
   mix(ints, sizeof(ints));
   mix(&c.rope_theta, sizeof(double));
   mix(&c.softmax_scale, sizeof(double));
@@ -116,9 +121,14 @@ uint64_t config_hash(const wf_config& c) {
 
 size_t pool_bytes(const Shape& sh) { return size_t(sh.L) * sh.n_slots * sh.page_bytes; }
 size_t anchor_bytes(const Shape& sh) { return size_t(sh.L) * sh.anchor_page_bytes; }
+size_t rope_hw_offset(const Shape& sh) { return (size_t(sh.nt) * sizeof(double) + 15) / 16 * 16; }
 size_t rope_table_bytes(const Shape& sh) {
-  return (size_t(sh.n_frames) * sh.nt + size_t(sh.Hh) * sh.nh + size_t(sh.Ww) * sh.nw) *
-         2 * sizeof(float);
+  return rope_hw_offset(sh) + (size_t(sh.Hh) * sh.nh + size_t(sh.Ww) * sh.nw) * 2 * sizeof(float);
+}
+bool round_in_range(const Shape& sh, int64_t k) {
+  if (k < 0) return false;
+  if (sh.unbounded) return int64_t(sh.F) * (k + 1) <= sh.max_frames;
+  return k < int64_t(sh.n_chunk) + sh.S;
 }
 // Two halves per split group: O [N][H][D] and (e, l) [N][H] in fp32.
 size_t split_scratch_bytes(const Shape& sh) {

@@ -18,10 +18,11 @@ namespace wf {
 // Everything the library derives once from a validated wf_config.
 struct Shape {
   int S, W, Ws, Wmax, ring, anchor, n_chunk;
+  bool unbounded;              // n_chunk <= 0: a stream, every chunk >= 0 exists
+  int max_frames;              // unbounded: frames the stream may reach
   int F, Hh, Ww, H, D, L, N;   // N = tokens per chunk
   int n_slots;                 // 4 + Wmax + 2 S
   int nt, nh, nw;              // RoPE pairs per axis (frame, row, column)
-  int n_frames;                // frame positions covered by the tables
   int dtype, mask;
   double theta, scale;
   size_t elem;                 // bytes per element of q/k/v/q_rot/out
@@ -42,7 +43,10 @@ bool derive_shape(const wf_config* cfg, Shape* out, std::string* why);
 // FNV-1a over the config fields that change a plan or a launch.
 uint64_t config_hash(const wf_config& cfg);
 
-// Builds the plan of round k (caller checked 0 <= k < n_chunk + S).
+// Round k exists: 0 <= k < n_chunk + S, or F (k + 1) <= max_frames when unbounded.
+bool round_in_range(const Shape& sh, int64_t k);
+
+// Builds the plan of round k (caller checked round_in_range).
 void build_plan(const Shape& sh, uint64_t hash, int64_t k, wf_plan* out);
 
 // Slot ring (closed form; ring = Wmax + 2):
@@ -62,10 +66,14 @@ inline int slot_denoise(const Shape& sh, int64_t k, int j) {
 constexpr int kMaxSplit = 2;
 
 // Bytes of caller buffers.  The table buffer holds the RoPE tables
-// (rope_table_bytes, rounded up to 256) and then the split scratch.
+// (rope_table_bytes, rounded up to 256) and then the split scratch.  The
+// RoPE part is the frame-axis frequencies (nt doubles, padded to 16 bytes)
+// and the row and column cos/sin tables; rope_hw_offset is where the latter
+// start.
 size_t pool_bytes(const Shape& sh);
 size_t anchor_bytes(const Shape& sh);
 size_t rope_table_bytes(const Shape& sh);
+size_t rope_hw_offset(const Shape& sh);
 size_t split_scratch_bytes(const Shape& sh);
 size_t table_bytes(const Shape& sh);
 // Byte offsets inside one pool page: Vt after K, then (FP8 / FP8K) the codes.

@@ -7,10 +7,21 @@
 // App. B.3: chunk 0's unrotated key is kept so RoPE can be re-applied when
 // the window shifts (TASK_CAPTURE / TASK_ANCHOR).
 //
-// Grid: (token blocks of 64, heads, tasks).  One work-group moves one
-// 64-token x D block of one head: 16-byte global loads and stores, RoPE in
-// fp32 from fp32 cos/sin tables, V transposed through LDS so the page's Vt
-// rows (keys contiguous) are written with full 16-byte stores.
+// Grid: (64-token blocks, head groups, tasks).  A work-group owns one block
+// of 64 tokens of one task and a group of heads, which it walks a few heads
+// at a time.  A thread owns 8 consecutive tokens x one 16-byte chunk of a
+// head row (8 bf16 / 4 fp32 elements):
+//   * its rotation angles depend on the token and the pair, not on the head,
+//     so the thread forms its cos/sin once and reuses them for every head of
+//     the group;
+//   * the frame-axis cos/sin come from the absolute frame position, computed
+//     in fp64 per work-group (frames x pairs of the block), so positions are
+//     not bounded by the length of a table; the row and column tables are
+//     fixed (Hh and Ww positions);
+//   * the thread's 8 x 8 (bf16) block of V is transposed in registers, so the
+//     page's Vt rows (keys contiguous) are written with 16-byte stores; eight
+//     consecutive lanes own the 8 token groups of one chunk, which makes every
+//     load and store a 128-byte contiguous segment.
 // HBM-bound: every byte is read once and written once.
 #include <hip/hip_runtime.h>
 
@@ -21,174 +32,210 @@ namespace {
 
 constexpr int kTokens = 64;    // tokens per work-group
 constexpr int kThreads = 256;
-constexpr int kMaxD = 128;
+constexpr int kRows = 8;       // consecutive tokens per thread
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <typename T>
 struct Vec;
 template <>
 struct Vec<float> {
   static constexpr int n = 4;
-  typedef float raw __attribute__((ext_vector_type(4)));
-  __device__ static float get(const raw& r, int e) { return r[e]; }
-  __device__ static void set(raw& r, int e, float x) { r[e] = x; }
+  typedef f32x4 raw;
 };
 template <>
 struct Vec<__bf16> {
   static constexpr int n = 8;
-  typedef __bf16 raw __attribute__((ext_vector_type(8)));
-  __device__ static float get(const raw& r, int e) { return static_cast<float>(r[e]); }
-  __device__ static void set(raw& r, int e, float x) { r[e] = static_cast<__bf16>(x); }
+  typedef bf16x8 raw;
 };
 
-// Rotates the VEC elements starting at element d0 of one token row.
-template <typename T>
-__device__ inline typename Vec<T>::raw rope_chunk(const typename Vec<T>::raw& x, int d0,
-                                                  int frame, int y, int xcol,
-                                                  const PublishArgs& a) {
-  using V = Vec<T>;
-  typename V::raw out;
-  const float2* tf = a.rope;
-  const float2* th = tf + static_cast<int64_t>(a.n_frames) * a.nt;
-  const float2* tw = th + a.Hh * a.nh;
-#pragma unroll
-  for (int e = 0; e < V::n; e += 2) {
-    const int p = (d0 + e) >> 1;
-    float2 cs;
-    if (p < a.nt) {
-      cs = tf[static_cast<int64_t>(frame) * a.nt + p];
-    } else if (p < a.nt + a.nh) {
-      cs = th[y * a.nh + (p - a.nt)];
-    } else {
-      cs = tw[xcol * a.nw + (p - a.nt - a.nh)];
-    }
-    const float x0 = V::get(x, e), x1 = V::get(x, e + 1);
-    V::set(out, e, x0 * cs.x - x1 * cs.y);
-    V::set(out, e + 1, x0 * cs.y + x1 * cs.x);
+// The thread's place in a work-group: item = 8 tokens x one 16-byte chunk of
+// one head; lanes 8 c + g own chunk c of token group g.
+struct Geom {
+  int hpp;    // heads a pass of the work-group covers
+  int slot;   // head of this thread within a pass (>= hpp: idle)
+  int g, c;   // token group (tokens 8 g .. 8 g + 7 of the block), chunk
+};
+
+__device__ inline Geom geom(int D, int vec) {
+  Geom q;
+  const int ipt = kRows * (D / vec);
+  q.hpp = kThreads / ipt;
+  const int t = threadIdx.x;
+  q.slot = t / ipt;
+  const int it = t - q.slot * ipt;
+  q.c = it >> 3;
+  q.g = it & 7;
+  return q;
+}
+
+// cos/sin of the frame-axis pairs at every frame the block's tokens span:
+// angle = (frame0 + f) * omega_m in fp64, rounded to fp32.  ftab[f * nt + m].
+__device__ inline int frame_table(const PublishArgs& a, int frame0, int tok0, float2* ftab) {
+  const int hw = a.Hh * a.Ww;
+  const int last = min(tok0 + kTokens, a.N) - 1;
+  const int f_lo = tok0 / hw;
+  const int n = (last / hw - f_lo + 1) * a.nt;
+  for (int i = threadIdx.x; i < n; i += kThreads) {
+    const int f = i / a.nt, m = i - f * a.nt;
+    const double ang = static_cast<double>(static_cast<int64_t>(frame0) + f_lo + f) * a.omega_t[m];
+    double s, c;
+    sincos(ang, &s, &c);
+    ftab[i] = make_float2(static_cast<float>(c), static_cast<float>(s));
   }
+  return f_lo;
+}
+
+// cos/sin of this thread's pairs (VEC / 2 per token) for its 8 tokens.
+template <int VEC>
+__device__ inline void thread_angles(const PublishArgs& a, const float2* ftab, int f_lo, int t0,
+                                     int c, float2 (&cs)[kRows][VEC / 2]) {
+  const float2* th = a.rope_hw;              // [Hh][nh]
+  const float2* tw = th + a.Hh * a.nh;       // [Ww][nw]
+  const int hw = a.Hh * a.Ww;
+#pragma unroll
+  for (int i = 0; i < kRows; ++i) {
+    const int tok = min(t0 + i, a.N - 1);    // rows past N are never stored
+    const int f = tok / hw - f_lo, y = (tok / a.Ww) % a.Hh, x = tok % a.Ww;
+#pragma unroll
+    for (int e = 0; e < VEC / 2; ++e) {
+      const int p = (c * VEC >> 1) + e;
+      if (p < a.nt) {
+        cs[i][e] = ftab[f * a.nt + p];
+      } else if (p < a.nt + a.nh) {
+        cs[i][e] = th[y * a.nh + (p - a.nt)];
+      } else {
+        cs[i][e] = tw[x * a.nw + (p - a.nt - a.nh)];
+      }
+    }
+  }
+}
+
+// Rotated pairs (x_2e, x_2e+1) -> (x0 cos - x1 sin, x0 sin + x1 cos), fp32.
+template <int VEC, typename R>
+__device__ inline void rotate_f32(const R& x, const float2 (&cs)[VEC / 2], float (&out)[VEC]) {
+#pragma unroll
+  for (int e = 0; e < VEC / 2; ++e) {
+    const float x0 = static_cast<float>(x[2 * e]), x1 = static_cast<float>(x[2 * e + 1]);
+    out[2 * e] = x0 * cs[e].x - x1 * cs[e].y;
+    out[2 * e + 1] = x0 * cs[e].y + x1 * cs[e].x;
+  }
+}
+
+template <typename T>
+__device__ inline typename Vec<T>::raw rotate(const typename Vec<T>::raw& x,
+                                              const float2 (&cs)[Vec<T>::n / 2]) {
+  constexpr int VEC = Vec<T>::n;
+  float r[VEC];
+  rotate_f32<VEC>(x, cs, r);
+  typename Vec<T>::raw out;
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) out[e] = static_cast<T>(r[e]);
   return out;
 }
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void wf_publish_kernel(const PublishArgs a) {
-  using V = Vec<T>;
-  using raw = typename V::raw;
-  constexpr int VEC = V::n;
-  // V block staged for the transpose; the +2 element pad spreads rows over
-  // LDS banks when a column is gathered.
-  __shared__ T vtile[kTokens][kMaxD + 2];
+  using raw = typename Vec<T>::raw;
+  constexpr int VEC = Vec<T>::n;
+  constexpr int kPieces = kRows / VEC;          // 16-byte pieces of 8 tokens
+  __shared__ float2 ftab[kMaxFrameEntries];
 
   const PublishTask task = a.task[blockIdx.z];
-  const int h = blockIdx.y;
   const int tok0 = blockIdx.x * kTokens;
+  const int hg0 = blockIdx.y * a.heads_per_group;
+  const int hg1 = min(a.H, hg0 + a.heads_per_group);
   const int N = a.N, H = a.H, D = a.D;
-  const int cpr = D / VEC;                       // 16-byte chunks per row
-  const int64_t hnd = static_cast<int64_t>(H) * N * D;
-  T* page = static_cast<T*>(a.pool) + static_cast<int64_t>(task.slot) * a.page_elems;
-  T* pageK = page;                               // [H][N][D]
-  T* pageVt = page + hnd;                        // [H][D][N]
-  T* anc = static_cast<T*>(a.anchor_raw);
-  T* ancK = anc;
-  T* ancVt = anc + hnd;
-  const int hw = a.Hh * a.Ww;
-
-  if (task.mode == TASK_ANCHOR) {
-    // Key: re-rotate the kept raw key at the anchor's current position.
-    for (int idx = threadIdx.x; idx < kTokens * cpr; idx += kThreads) {
-      const int r = idx / cpr, c = idx - r * cpr;
-      const int tok = tok0 + r;
-      if (tok >= N) continue;
-      const int64_t off = (static_cast<int64_t>(h) * N + tok) * D + c * VEC;
-      const raw x = *reinterpret_cast<const raw*>(ancK + off);
-      const int f = tok / hw, y = (tok / a.Ww) % a.Hh, xc = tok % a.Ww;
-      *reinterpret_cast<raw*>(pageK + off) = rope_chunk<T>(x, c * VEC, task.frame0 + f, y, xc, a);
-    }
-    // Value: copied unchanged (Vt rows of this token block).
-    const int gpr = kTokens / VEC;
-    for (int idx = threadIdx.x; idx < D * gpr; idx += kThreads) {
-      const int d = idx / gpr, g = idx - d * gpr;
-      const int tok = tok0 + g * VEC;
-      if (tok >= N) continue;
-      const int64_t off = (static_cast<int64_t>(h) * D + d) * N + tok;
-      *reinterpret_cast<raw*>(pageVt + off) = *reinterpret_cast<const raw*>(ancVt + off);
-    }
-    return;
-  }
-
-  const bool capture = task.mode == TASK_CAPTURE;
-  const T* q = static_cast<const T*>(a.q);
-  const T* k = static_cast<const T*>(a.k);
-  const T* v = static_cast<const T*>(a.v);
-  T* qr = static_cast<T*>(a.q_rot);
-  const int64_t stage_base = static_cast<int64_t>(task.stage) * N;
-
-  for (int idx = threadIdx.x; idx < kTokens * cpr; idx += kThreads) {
-    const int r = idx / cpr, c = idx - r * cpr;
-    const int tok = tok0 + r;
-    if (tok >= N) continue;
-    const int64_t in = ((stage_base + tok) * H + h) * D + c * VEC;
-    const int f = tok / hw, y = (tok / a.Ww) % a.Hh, xc = tok % a.Ww;
-    const int frame = task.frame0 + f;
-    const raw xq = *reinterpret_cast<const raw*>(q + in);
-    const raw xk = *reinterpret_cast<const raw*>(k + in);
-    const raw xv = *reinterpret_cast<const raw*>(v + in);
-    *reinterpret_cast<raw*>(qr + in) = rope_chunk<T>(xq, c * VEC, frame, y, xc, a);
-    const int64_t kofs = (static_cast<int64_t>(h) * N + tok) * D + c * VEC;
-    *reinterpret_cast<raw*>(pageK + kofs) = rope_chunk<T>(xk, c * VEC, frame, y, xc, a);
-    if (capture) *reinterpret_cast<raw*>(ancK + kofs) = xk;
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) vtile[r][c * VEC + e] = static_cast<T>(V::get(xv, e));
-  }
+  const Geom q = geom(D, VEC);
+  const int f_lo = frame_table(a, task.frame0, tok0, ftab);
   __syncthreads();
-  // Transposed write: VEC consecutive tokens of one value dimension.
-  const int gpr = kTokens / VEC;
-  for (int idx = threadIdx.x; idx < D * gpr; idx += kThreads) {
-    const int d = idx / gpr, g = idx - d * gpr;
-    const int tok = tok0 + g * VEC;
-    if (tok >= N) continue;
-    raw o;
+  if (q.slot >= q.hpp) return;
+  float2 cs[kRows][VEC / 2];
+  const int t0 = tok0 + kRows * q.g;
+  thread_angles<VEC>(a, ftab, f_lo, t0, q.c, cs);
+
+  const int64_t hnd = static_cast<int64_t>(H) * N * D;
+  T* pageK = static_cast<T*>(a.pool) + static_cast<int64_t>(task.slot) * a.page_elems;  // [H][N][D]
+  T* pageVt = pageK + hnd;                                                             // [H][D][N]
+  T* ancK = static_cast<T*>(a.anchor_raw);
+  T* ancVt = ancK + hnd;
+  const bool capture = task.mode == TASK_CAPTURE;
+
+  for (int h = hg0 + q.slot; h < hg1; h += q.hpp) {
+    const int64_t krow = (static_cast<int64_t>(h) * N + t0) * D + VEC * q.c;   // K[h][t0][VEC c]
+    const int64_t vrow = (static_cast<int64_t>(h) * D + VEC * q.c) * N + t0;   // Vt[h][VEC c][t0]
+    if (task.mode == TASK_ANCHOR) {
+      // Key: the kept raw key re-rotated at the anchor's current position.
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) V::set(o, e, static_cast<float>(vtile[g * VEC + e][d]));
-    const int64_t off = (static_cast<int64_t>(h) * D + d) * N + tok;
-    *reinterpret_cast<raw*>(pageVt + off) = o;
-    if (capture) *reinterpret_cast<raw*>(ancVt + off) = o;
+      for (int i = 0; i < kRows; ++i) {
+        if (t0 + i >= N) break;
+        const raw x = *reinterpret_cast<const raw*>(ancK + krow + int64_t(i) * D);
+        *reinterpret_cast<raw*>(pageK + krow + int64_t(i) * D) = rotate<T>(x, cs[i]);
+      }
+      // Value: the kept Vt rows copied unchanged.
+#pragma unroll
+      for (int e = 0; e < VEC; ++e)
+#pragma unroll
+        for (int j = 0; j < kPieces; ++j) {
+          if (t0 + VEC * j >= N) break;
+          const int64_t off = vrow + int64_t(e) * N + VEC * j;
+          *reinterpret_cast<raw*>(pageVt + off) = *reinterpret_cast<const raw*>(ancVt + off);
+        }
+      continue;
+    }
+    const T* qin = static_cast<const T*>(a.q);
+    const T* kin = static_cast<const T*>(a.k);
+    const T* vin = static_cast<const T*>(a.v);
+    T* qr = static_cast<T*>(a.q_rot);
+    const int64_t in0 = ((static_cast<int64_t>(task.stage) * N + t0) * H + h) * D + VEC * q.c;
+    const int64_t in_step = static_cast<int64_t>(H) * D;
+    raw xq[kRows], xk[kRows], xv[kRows];
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) {
+      if (t0 + i < N) {
+        xq[i] = *reinterpret_cast<const raw*>(qin + in0 + i * in_step);
+        xk[i] = *reinterpret_cast<const raw*>(kin + in0 + i * in_step);
+        xv[i] = *reinterpret_cast<const raw*>(vin + in0 + i * in_step);
+      } else {
+        xq[i] = raw{};
+        xk[i] = raw{};
+        xv[i] = raw{};
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) {
+      if (t0 + i >= N) break;
+      *reinterpret_cast<raw*>(qr + in0 + i * in_step) = rotate<T>(xq[i], cs[i]);
+      *reinterpret_cast<raw*>(pageK + krow + int64_t(i) * D) = rotate<T>(xk[i], cs[i]);
+      if (capture) *reinterpret_cast<raw*>(ancK + krow + int64_t(i) * D) = xk[i];
+    }
+    // Transposed write: element e of the chunk is value dim VEC c + e; its
+    // 8 tokens go out as kPieces 16-byte pieces.
+#pragma unroll
+    for (int e = 0; e < VEC; ++e)
+#pragma unroll
+      for (int j = 0; j < kPieces; ++j) {
+        if (t0 + VEC * j >= N) break;
+        raw o;
+#pragma unroll
+        for (int u = 0; u < VEC; ++u) o[u] = xv[VEC * j + u][e];
+        const int64_t off = vrow + int64_t(e) * N + VEC * j;
+        *reinterpret_cast<raw*>(pageVt + off) = o;
+        if (capture) *reinterpret_cast<raw*>(ancVt + off) = o;
+      }
   }
 }
 
 // ---------------------------------------------------------------- FP8 ----
-// FP8 pages ("Wave Forcing" App. C.6: 8-bit K/V halve the payload).  One
-// work-group quantises one 64-token tile of one head: rotated K and V each
-// get one power-of-two scale 2^e with e the smallest integer such that
-// amax(tile) <= 448 * 2^e, and are stored as OCP E4M3 codes of x / 2^e
-// (round to nearest even).  q_rot stays bf16.  Tokens N..Npad-1 are zero.
-// With kBf16V (the 8-bit QK^T tier) only K is quantised; Vt is written in
-// bf16 (its scale code stays 2^0).
+// FP8 pages ("Wave Forcing" App. C.6: 8-bit K/V halve the payload).  A
+// work-group owns one 64-token tile (blockIdx.x) of a group of heads, two
+// heads per pass.  Rotated K and V of each (tile, head) get one power-of-two
+// scale 2^e each, e the smallest integer with amax(tile) <= 448 * 2^e, and
+// are stored as OCP E4M3 codes of x / 2^e (round to nearest even).  q_rot
+// stays bf16.  Tokens N..Npad-1 are zero.  With kBf16V (the 8-bit QK^T
+// tier) only K is quantised; Vt is written in bf16 (its scale code is 2^0).
 constexpr int kFp8D = 128;
-constexpr int kFp8Items = kTokens * (kFp8D / 8) / kThreads;   // (row, 8-dim chunk) per thread
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-
-// RoPE of 8 consecutive elements starting at d0 (even), fp32 result.
-__device__ inline void rope8_f32(const bf16x8& x, int d0, int frame, int y, int xcol,
-                                 const PublishArgs& a, float out[8]) {
-  const float2* tf = a.rope;
-  const float2* th = tf + static_cast<int64_t>(a.n_frames) * a.nt;
-  const float2* tw = th + a.Hh * a.nh;
-#pragma unroll
-  for (int e = 0; e < 8; e += 2) {
-    const int p = (d0 + e) >> 1;
-    float2 cs;
-    if (p < a.nt) {
-      cs = tf[static_cast<int64_t>(frame) * a.nt + p];
-    } else if (p < a.nt + a.nh) {
-      cs = th[y * a.nh + (p - a.nt)];
-    } else {
-      cs = tw[xcol * a.nw + (p - a.nt - a.nh)];
-    }
-    const float x0 = static_cast<float>(x[e]), x1 = static_cast<float>(x[e + 1]);
-    out[e] = x0 * cs.x - x1 * cs.y;
-    out[e + 1] = x0 * cs.y + x1 * cs.x;
-  }
-}
 
 // Smallest e with amax <= 448 * 2^e (0 for amax == 0), exactly: with
 // amax = m 2^x, m in [0.5, 1), 448 * 2^e = 0.875 * 2^(e + 9).
@@ -201,7 +248,7 @@ __device__ inline int fp8_exponent(float amax) {
 }
 
 // Eight floats (already divided by the scale, |x| <= 448) as E4M3 codes.
-__device__ inline uint2 fp8_pack8(const float v[8]) {
+__device__ inline uint2 fp8_pack8(const float (&v)[8]) {
   uint2 r;
   r.x = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
   r.x = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], r.x, true);
@@ -218,161 +265,184 @@ __device__ inline float wave_max(float v) {
 
 template <bool kBf16V>
 __global__ __launch_bounds__(kThreads) void wf_publish_fp8_kernel(const PublishArgs a) {
-  // V tile staged token-major in fp32 for the amax and the transposed write.
-  __shared__ float vtile[kTokens][kFp8D + 1];
-  __shared__ float red[2][kThreads / 64];
+  constexpr int D = kFp8D;
+  __shared__ float2 ftab[kMaxFrameEntries];
+  __shared__ float red[kThreads / 64][2];
 
   const PublishTask task = a.task[blockIdx.z];
-  const int h = blockIdx.y;
   const int tile = blockIdx.x;
   const int tok0 = tile * kTokens;
+  const int hg0 = blockIdx.y * a.heads_per_group;
+  const int hg1 = min(a.H, hg0 + a.heads_per_group);
   const int N = a.N, H = a.H, Np = a.Npad;
-  constexpr int D = kFp8D;
-  const int tid = threadIdx.x;
+  const Geom q = geom(D, 8);                    // two heads per pass, 2 waves each
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int f_lo = frame_table(a, task.frame0, tok0, ftab);
+  __syncthreads();
+  float2 cs[kRows][4];
+  const int t0 = tok0 + kRows * q.g;
+  thread_angles<8>(a, ftab, f_lo, t0, q.c, cs);
+
   uint8_t* page = static_cast<uint8_t*>(a.pool) + static_cast<int64_t>(task.slot) * a.page_bytes;
-  uint8_t* K8 = page;                                             // [H][Np][D]
-  uint8_t* V8 = page + static_cast<int64_t>(H) * Np * D;          // [H][D][Np] (bf16 with kBf16V)
+  uint8_t* K8 = page;                                                      // [H][Np][D]
+  uint8_t* V8 = page + static_cast<int64_t>(H) * Np * D;                   // [H][D][Np]
   uint8_t* codes = page + (kBf16V ? 3 : 2) * static_cast<int64_t>(H) * Np * D;   // [H][T][2]
   const int64_t hnd = static_cast<int64_t>(H) * N * D;
-  __bf16* ancK = static_cast<__bf16*>(a.anchor_raw);              // bf16 [H][N][D]
-  __bf16* ancVt = ancK + hnd;                                     // bf16 [H][D][N]
-  const int hw = a.Hh * a.Ww;
+  __bf16* ancK = static_cast<__bf16*>(a.anchor_raw);                       // bf16 [H][N][D]
+  __bf16* ancVt = ancK + hnd;                                              // bf16 [H][D][N]
+  const bool capture = task.mode == TASK_CAPTURE;
+  const bool anchor = task.mode == TASK_ANCHOR;
 
-  float kr[kFp8Items][8];
-  float kmax = 0.f, vmax = 0.f;
-  if (task.mode == TASK_ANCHOR) {
-    // anchor: re-rotate the kept raw key; the kept Vt is re-quantised
+  for (int hb = hg0; hb < hg1; hb += q.hpp) {   // uniform over the work-group
+    const int h = hb + q.slot;
+    const bool act = h < hg1;
+    float kr[kRows][8];                         // rotated keys (0 past N)
+    bf16x8 vt[8];                               // values, dim-major: vt[e][i] = v(t0 + i, 8 c + e)
+    float kmax = 0.f, vmax = 0.f;
+    const int64_t krow = (static_cast<int64_t>(h) * N + t0) * D + 8 * q.c;
+    const int64_t vrow = (static_cast<int64_t>(h) * D + 8 * q.c) * N + t0;
+    if (act && anchor) {
 #pragma unroll
-    for (int i = 0; i < kFp8Items; ++i) {
-      const int idx = tid + i * kThreads, r = idx >> 4, c = idx & 15;
-      const int tok = tok0 + r;
+      for (int i = 0; i < kRows; ++i) {
+        if (t0 + i < N) {
+          const bf16x8 x = *reinterpret_cast<const bf16x8*>(ancK + krow + int64_t(i) * D);
+          rotate_f32<8>(x, cs[i], kr[i]);
+        } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) kr[i][e] = 0.f;
-      if (tok < N) {
-        const bf16x8 x = *reinterpret_cast<const bf16x8*>(ancK + (static_cast<int64_t>(h) * N + tok) * D + 8 * c);
-        const int f = tok / hw, y = (tok / a.Ww) % a.Hh, xc = tok % a.Ww;
-        rope8_f32(x, 8 * c, task.frame0 + f, y, xc, a, kr[i]);
+          for (int e = 0; e < 8; ++e) kr[i][e] = 0.f;   // padding: +0 codes (a rotated 0 may be -0)
+        }
       }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) kmax = fmaxf(kmax, fabsf(kr[i][e]));
-    }
-#pragma unroll
-    for (int i = 0; i < kFp8Items; ++i) {
-      const int idx = tid + i * kThreads, d = idx >> 3, g = idx & 7;
-      const int tok = tok0 + 8 * g;     // N % 8 == 0: a group is all real or all padding
-      bf16x8 x = {};
-      if (tok < N) x = *reinterpret_cast<const bf16x8*>(ancVt + (static_cast<int64_t>(h) * D + d) * N + tok);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float v = static_cast<float>(x[e]);
-        vtile[8 * g + e][d] = v;
-        vmax = fmaxf(vmax, fabsf(v));
+        vt[e] = bf16x8{};
+        if (t0 < N) vt[e] = *reinterpret_cast<const bf16x8*>(ancVt + vrow + int64_t(e) * N);
       }
+    } else if (act) {
+      const __bf16* qin = static_cast<const __bf16*>(a.q);
+      const __bf16* kin = static_cast<const __bf16*>(a.k);
+      const __bf16* vin = static_cast<const __bf16*>(a.v);
+      __bf16* qr = static_cast<__bf16*>(a.q_rot);
+      const int64_t in0 = ((static_cast<int64_t>(task.stage) * N + t0) * H + h) * D + 8 * q.c;
+      const int64_t in_step = static_cast<int64_t>(H) * D;
+      bf16x8 xq[kRows], xk[kRows], xv[kRows];
+#pragma unroll
+      for (int i = 0; i < kRows; ++i) {
+        xq[i] = bf16x8{};
+        xk[i] = bf16x8{};
+        xv[i] = bf16x8{};
+        if (t0 + i < N) {
+          xq[i] = *reinterpret_cast<const bf16x8*>(qin + in0 + i * in_step);
+          xk[i] = *reinterpret_cast<const bf16x8*>(kin + in0 + i * in_step);
+          xv[i] = *reinterpret_cast<const bf16x8*>(vin + in0 + i * in_step);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kRows; ++i) {
+        if (t0 + i < N) {
+          rotate_f32<8>(xk[i], cs[i], kr[i]);
+          *reinterpret_cast<bf16x8*>(qr + in0 + i * in_step) = rotate<__bf16>(xq[i], cs[i]);
+          if (capture) *reinterpret_cast<bf16x8*>(ancK + krow + int64_t(i) * D) = xk[i];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) kr[i][e] = 0.f;   // padding: +0 codes (a rotated 0 may be -0)
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int i = 0; i < kRows; ++i) vt[e][i] = xv[i][e];
+    } else {
+#pragma unroll
+      for (int i = 0; i < kRows; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kr[i][e] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vt[e] = bf16x8{};
     }
-  } else {
-    const bool capture = task.mode == TASK_CAPTURE;
-    const __bf16* q = static_cast<const __bf16*>(a.q);
-    const __bf16* k = static_cast<const __bf16*>(a.k);
-    const __bf16* v = static_cast<const __bf16*>(a.v);
-    __bf16* qr = static_cast<__bf16*>(a.q_rot);
-    const int64_t stage_base = static_cast<int64_t>(task.stage) * N;
 #pragma unroll
-    for (int i = 0; i < kFp8Items; ++i) {
-      const int idx = tid + i * kThreads, r = idx >> 4, c = idx & 15;
-      const int tok = tok0 + r;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) kr[i][e] = 0.f;
-      bf16x8 xv = {};
-      if (tok < N) {
-        const int64_t in = ((stage_base + tok) * H + h) * D + 8 * c;
-        const int f = tok / hw, y = (tok / a.Ww) % a.Hh, xc = tok % a.Ww;
-        const int frame = task.frame0 + f;
-        const bf16x8 xq = *reinterpret_cast<const bf16x8*>(q + in);
-        const bf16x8 xk = *reinterpret_cast<const bf16x8*>(k + in);
-        xv = *reinterpret_cast<const bf16x8*>(v + in);
-        float qv[8];
-        rope8_f32(xq, 8 * c, frame, y, xc, a, qv);
-        bf16x8 qo;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qo[e] = static_cast<__bf16>(qv[e]);
-        *reinterpret_cast<bf16x8*>(qr + in) = qo;
-        rope8_f32(xk, 8 * c, frame, y, xc, a, kr[i]);
-        if (capture) *reinterpret_cast<bf16x8*>(ancK + (static_cast<int64_t>(h) * N + tok) * D + 8 * c) = xk;
-      }
+    for (int i = 0; i < kRows; ++i)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         kmax = fmaxf(kmax, fabsf(kr[i][e]));
-        const float vf = static_cast<float>(xv[e]);
-        vtile[r][8 * c + e] = vf;
-        vmax = fmaxf(vmax, fabsf(vf));
+        vmax = fmaxf(vmax, fabsf(static_cast<float>(vt[e][i])));
+      }
+    // tile amax of K and V over the head's two waves
+    kmax = wave_max(kmax);
+    vmax = wave_max(vmax);
+    if (lane == 0) {
+      red[wave][0] = kmax;
+      red[wave][1] = vmax;
+    }
+    __syncthreads();
+    const int w0 = wave & ~1;
+    kmax = fmaxf(red[w0][0], red[w0 + 1][0]);
+    vmax = fmaxf(red[w0][1], red[w0 + 1][1]);
+    if (act) {
+      const int ek = fp8_exponent(kmax), ev = kBf16V ? 0 : fp8_exponent(vmax);
+      const float sk = ldexpf(1.f, -ek), sv = ldexpf(1.f, -ev);
+      // K rows (padding rows get zero codes)
+#pragma unroll
+      for (int i = 0; i < kRows; ++i) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = kr[i][e] * sk;
+        *reinterpret_cast<uint2*>(K8 + (static_cast<int64_t>(h) * Np + t0 + i) * D + 8 * q.c) = fp8_pack8(x);
+      }
+      // Vt rows: 8 consecutive tokens of one value dim
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int64_t off = (static_cast<int64_t>(h) * D + 8 * q.c + e) * Np + t0;
+        if (kBf16V) {
+          *reinterpret_cast<bf16x8*>(reinterpret_cast<__bf16*>(V8) + off) = vt[e];
+        } else {
+          float x[8];
+#pragma unroll
+          for (int i = 0; i < kRows; ++i) x[i] = static_cast<float>(vt[e][i]) * sv;
+          *reinterpret_cast<uint2*>(V8 + off) = fp8_pack8(x);
+        }
+        if (capture && t0 < N) *reinterpret_cast<bf16x8*>(ancVt + vrow + int64_t(e) * N) = vt[e];
+      }
+      if (q.g == 0 && q.c == 0) {
+        const uint16_t code = static_cast<uint16_t>((ek + 127) | ((ev + 127) << 8));
+        *reinterpret_cast<uint16_t*>(codes + (static_cast<int64_t>(h) * a.T + tile) * 2) = code;
       }
     }
+    __syncthreads();                            // red is rewritten by the next pass
   }
-  // tile amax of K and V over the work-group
-  kmax = wave_max(kmax);
-  vmax = wave_max(vmax);
-  if ((tid & 63) == 0) {
-    red[0][tid >> 6] = kmax;
-    red[1][tid >> 6] = vmax;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int w = 0; w < kThreads / 64; ++w) {
-    kmax = fmaxf(kmax, red[0][w]);
-    vmax = fmaxf(vmax, red[1][w]);
-  }
-  const int ek = fp8_exponent(kmax), ev = kBf16V ? 0 : fp8_exponent(vmax);
-  const float sk = ldexpf(1.f, -ek), sv = ldexpf(1.f, -ev);
+}
 
-  // K rows: 8 codes per (row, chunk); padding rows are zero codes
-#pragma unroll
-  for (int i = 0; i < kFp8Items; ++i) {
-    const int idx = tid + i * kThreads, r = idx >> 4, c = idx & 15;
-    float x[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = kr[i][e] * sk;
-    *reinterpret_cast<uint2*>(K8 + (static_cast<int64_t>(h) * Np + tok0 + r) * D + 8 * c) = fp8_pack8(x);
-  }
-  // Vt rows: 8 consecutive tokens of one value dimension
-#pragma unroll
-  for (int i = 0; i < kFp8Items; ++i) {
-    const int idx = tid + i * kThreads, d = idx >> 3, g = idx & 7;
-    if (kBf16V) {
-      bf16x8 o;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = static_cast<__bf16>(vtile[8 * g + e][d]);
-      *reinterpret_cast<bf16x8*>(reinterpret_cast<__bf16*>(V8) + (static_cast<int64_t>(h) * D + d) * Np + tok0 + 8 * g) = o;
-    } else {
-      float x[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = vtile[8 * g + e][d] * sv;
-      const uint2 o = fp8_pack8(x);
-      *reinterpret_cast<uint2*>(V8 + (static_cast<int64_t>(h) * D + d) * Np + tok0 + 8 * g) = o;
-    }
-    if (task.mode == TASK_CAPTURE && tok0 + 8 * g < N) {
-      bf16x8 raw;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) raw[e] = static_cast<__bf16>(vtile[8 * g + e][d]);
-      *reinterpret_cast<bf16x8*>(ancVt + (static_cast<int64_t>(h) * D + d) * N + tok0 + 8 * g) = raw;
-    }
-  }
-  if (tid == 0) {
-    const uint16_t code = static_cast<uint16_t>((ek + 127) | ((ev + 127) << 8));
-    *reinterpret_cast<uint16_t*>(codes + (static_cast<int64_t>(h) * a.T + tile) * 2) = code;
-  }
+// Heads per work-group: a multiple of the heads one pass covers, few enough
+// groups that each work-group reuses its angles over several heads, enough
+// that the grid holds about four work-groups per compute unit.
+int heads_per_group(int H, int hpp, int blocks) {
+  const int want_groups = (1024 + blocks - 1) / blocks;
+  const int max_groups = (H + hpp - 1) / hpp;
+  const int groups = want_groups < 1 ? 1 : (want_groups > max_groups ? max_groups : want_groups);
+  int hpg = (H + groups - 1) / groups;
+  hpg = (hpg + hpp - 1) / hpp * hpp;
+  return hpg;
 }
 
 }  // namespace
 
-hipError_t launch_publish(const PublishArgs& a, int dtype, hipStream_t stream) {
-  if (a.n_tasks <= 0) return hipSuccess;
+hipError_t launch_publish(const PublishArgs& args, int dtype, hipStream_t stream) {
+  if (args.n_tasks <= 0) return hipSuccess;
+  if (args.nt > kMaxFramePairs) return hipErrorInvalidValue;
+  PublishArgs a = args;
+  const int vec = dtype == WF_F32 ? 4 : 8;
+  const int hpp = kThreads / (kRows * (a.D / vec));
+  if (hpp < 1 || a.D % vec != 0) return hipErrorInvalidValue;
   if (dtype == WF_FP8 || dtype == WF_FP8K) {
-    const dim3 grid(a.T, a.H, a.n_tasks);
+    if (a.D != kFp8D) return hipErrorInvalidValue;
+    a.heads_per_group = heads_per_group(a.H, hpp, a.T * a.n_tasks);
+    const dim3 grid(a.T, (a.H + a.heads_per_group - 1) / a.heads_per_group, a.n_tasks);
     if (dtype == WF_FP8) hipLaunchKernelGGL(wf_publish_fp8_kernel<false>, grid, dim3(kThreads), 0, stream, a);
     else hipLaunchKernelGGL(wf_publish_fp8_kernel<true>, grid, dim3(kThreads), 0, stream, a);
     return hipGetLastError();
   }
-  const dim3 grid((a.N + kTokens - 1) / kTokens, a.H, a.n_tasks);
+  const int blocks = (a.N + kTokens - 1) / kTokens;
+  a.heads_per_group = heads_per_group(a.H, hpp, blocks * a.n_tasks);
+  const dim3 grid(blocks, (a.H + a.heads_per_group - 1) / a.heads_per_group, a.n_tasks);
   if (dtype == WF_BF16) {
     hipLaunchKernelGGL(wf_publish_kernel<__bf16>, grid, dim3(kThreads), 0, stream, a);
   } else {

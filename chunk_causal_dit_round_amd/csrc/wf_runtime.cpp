@@ -99,7 +99,8 @@ wf_status do_publish(wf_handle* h, const wf_plan& p, int layer, const void* q, c
   a.q_rot = q_rot;
   a.pool = layer_ptr(h->pool, size_t(sh.n_slots) * sh.page_bytes, layer);
   a.anchor_raw = layer_ptr(h->anchor, sh.anchor_page_bytes, layer);
-  a.rope = static_cast<const float2*>(h->tables);
+  a.omega_t = static_cast<const double*>(h->tables);
+  a.rope_hw = reinterpret_cast<const float2*>(static_cast<const char*>(h->tables) + wf::rope_hw_offset(sh));
   a.page_elems = static_cast<int64_t>(sh.page_elems);
   a.page_bytes = static_cast<int64_t>(sh.page_bytes);
   a.Npad = sh.Npad;
@@ -113,7 +114,6 @@ wf_status do_publish(wf_handle* h, const wf_plan& p, int layer, const void* q, c
   a.nt = sh.nt;
   a.nh = sh.nh;
   a.nw = sh.nw;
-  a.n_frames = sh.n_frames;
   int n = 0;
   for (int s = 0; s <= sh.S; ++s) {
     const wf_cell& c = p.cells[s];
@@ -347,7 +347,7 @@ using namespace wf::rt;
 
 extern "C" {
 
-const char* wf_strerror(wf_status s) {
+const char* wf_strerror(int32_t s) {
   switch (s) {
     case WF_OK: return "ok";
     case WF_EINVAL: return "invalid argument";
@@ -430,23 +430,27 @@ wf_status wf_bind(wf_handle* h, void* d_pool, size_t pool_bytes, void* d_anchor_
   const wf_status sup = check_supported(sh);
   if (sup != WF_OK) return sup;
 
-  // cos/sin of every (position, pair) per axis, computed in fp64.
-  std::vector<float> tab(wf::rope_table_bytes(sh) / sizeof(float));
+  // The frame axis's frequencies theta^(-m/nt) in fp64 (the kernels form
+  // the angle (frame * omega) and its cos/sin in fp64 on the device), then
+  // cos/sin of every (row, pair) and (column, pair), computed in fp64.
+  std::vector<unsigned char> tab(wf::rope_table_bytes(sh), 0);
+  double* omega = reinterpret_cast<double*>(tab.data());
+  for (int m = 0; m < sh.nt; ++m) omega[m] = std::pow(sh.theta, -double(m) / double(sh.nt));
+  float* hw = reinterpret_cast<float*>(tab.data() + wf::rope_hw_offset(sh));
   size_t at = 0;
   auto axis = [&](int n_pos, int n_pairs) {
     for (int pos = 0; pos < n_pos; ++pos) {
       for (int m = 0; m < n_pairs; ++m) {
         const double w = std::pow(sh.theta, -double(m) / double(n_pairs));
         const double ang = double(pos) * w;
-        tab[at++] = static_cast<float>(std::cos(ang));
-        tab[at++] = static_cast<float>(std::sin(ang));
+        hw[at++] = static_cast<float>(std::cos(ang));
+        hw[at++] = static_cast<float>(std::sin(ang));
       }
     }
   };
-  axis(sh.n_frames, sh.nt);
   axis(sh.Hh, sh.nh);
   axis(sh.Ww, sh.nw);
-  const hipError_t e = hipMemcpy(d_tables, tab.data(), tab.size() * sizeof(float), hipMemcpyHostToDevice);
+  const hipError_t e = hipMemcpy(d_tables, tab.data(), tab.size(), hipMemcpyHostToDevice);
   if (e != hipSuccess) return fail(WF_EDEVICE, std::string("table upload: ") + hipGetErrorString(e));
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) == hipSuccess &&
@@ -470,8 +474,12 @@ wf_status wf_set_attention_split(wf_handle* h, int32_t mode) {
 
 wf_status wf_round_plan(const wf_handle* h, int64_t k, wf_plan* out) {
   if (!h || !out) return fail(WF_EINVAL, "handle or out is NULL");
-  if (k < 0 || k >= int64_t(h->sh.n_chunk) + h->sh.S)
-    return fail(WF_ERANGE, "round " + std::to_string(k) + " outside [0, n_chunk + S)");
+  if (!wf::round_in_range(h->sh, k)) {
+    return fail(WF_ERANGE, h->sh.unbounded
+                               ? "round " + std::to_string(k) + " needs more than max_frames = " +
+                                     std::to_string(h->sh.max_frames) + " frames"
+                               : "round " + std::to_string(k) + " outside [0, n_chunk + S)");
+  }
   wf::build_plan(h->sh, h->hash, k, out);
   return ok();
 }
@@ -479,6 +487,30 @@ wf_status wf_round_plan(const wf_handle* h, int64_t k, wf_plan* out) {
 wf_status wf_next_round(const wf_handle* h, int64_t* k) {
   if (!h || !k) return fail(WF_EINVAL, "handle or out is NULL");
   *k = h->next_k;
+  return ok();
+}
+
+wf_status wf_finish_stream(wf_handle* h, int64_t n_chunk) {
+  if (!h) return fail(WF_EINVAL, "handle is NULL");
+  if (!h->sh.unbounded) return fail(WF_EINVAL, "the request is bounded (n_chunk >= 1); nothing to finish");
+  for (const uint8_t p : h->published)
+    if (p) return fail(WF_EORDER, "a layer of round " + std::to_string(h->next_k) + " is already published");
+  if (n_chunk < h->next_k || n_chunk < 1 || n_chunk > (int64_t(1) << 30)) {
+    return fail(WF_EINVAL, "n_chunk " + std::to_string(n_chunk) + " must be >= the next round " +
+                               std::to_string(h->next_k) + " and >= 1");
+  }
+  wf_config c = h->cfg;
+  c.n_chunk = static_cast<int32_t>(n_chunk);
+  c.max_frames = 0;
+  wf::Shape sh;
+  std::string why;
+  if (!wf::derive_shape(&c, &sh, &why)) return fail(WF_EINVAL, why);
+  if (wf::pool_bytes(sh) != wf::pool_bytes(h->sh) || wf::table_bytes(sh) != wf::table_bytes(h->sh) ||
+      wf::anchor_bytes(sh) != wf::anchor_bytes(h->sh))
+    return fail(WF_EINVAL, "buffer sizes would change");
+  h->cfg = c;
+  h->sh = sh;
+  h->hash = wf::config_hash(c);
   return ok();
 }
 

@@ -9,7 +9,9 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libwf.so")
+# WF_LIBRARY selects another build of the same library (the sanitizer build
+# of the CPU ABI tests); by default the in-tree libwf.so.
+LIB_PATH = os.environ.get("WF_LIBRARY") or os.path.join(_PKG, "libwf.so")
 
 WF_MAX_STAGES = 8
 WF_MAX_GROUPS = WF_MAX_STAGES + 1
@@ -27,7 +29,7 @@ i32, i64, u64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_d
 class wf_config(ctypes.Structure):
     _fields_ = [("S", i32), ("W", i32), ("W_store", i32), ("anchor", i32), ("n_chunk", i32),
                 ("F", i32), ("Hh", i32), ("Ww", i32), ("n_heads", i32), ("head_dim", i32),
-                ("n_layers", i32), ("dtype", i32), ("mask", i32), ("reserved", i32),
+                ("n_layers", i32), ("dtype", i32), ("mask", i32), ("max_frames", i32),
                 ("rope_theta", f64), ("softmax_scale", f64)]
 
 
@@ -96,6 +98,7 @@ def _load():
         "wf_round_plan": (i32, [H, i64, ctypes.POINTER(wf_plan)]),
         "wf_next_round": (i32, [H, ctypes.POINTER(i64)]),
         "wf_reset": (i32, [H]),
+        "wf_finish_stream": (i32, [H, i64]),
         "wf_kv_publish": (i32, [H, ctypes.POINTER(wf_plan), i32, cvp, cvp, cvp, vp, vp]),
         "wf_wave_attention": (i32, [H, ctypes.POINTER(wf_plan), i32, cvp, vp, vp]),
         "wf_wave_attention_noalloc": (i32, [H, ctypes.POINTER(wf_plan), i32, cvp, vp, vp]),
@@ -147,10 +150,12 @@ def _stream(stream):
 
 
 def make_config(S, W, n_chunk, F, Hh, Ww, n_heads, head_dim, n_layers, *, W_store=-1,
-                anchor=1, dtype=WF_BF16, mask=WF_MASK_WAVE, rope_theta=0.0, softmax_scale=0.0):
+                anchor=1, dtype=WF_BF16, mask=WF_MASK_WAVE, rope_theta=0.0, softmax_scale=0.0,
+                max_frames=0):
     return wf_config(S=S, W=W, W_store=W_store, anchor=anchor, n_chunk=n_chunk, F=F, Hh=Hh,
                      Ww=Ww, n_heads=n_heads, head_dim=head_dim, n_layers=n_layers, dtype=dtype,
-                     mask=mask, reserved=0, rope_theta=rope_theta, softmax_scale=softmax_scale)
+                     mask=mask, max_frames=max_frames, rope_theta=rope_theta,
+                     softmax_scale=softmax_scale)
 
 
 def wf_strerror(status):
@@ -202,6 +207,10 @@ def wf_next_round(h):
 
 def wf_reset(h):
     _check(_lib.wf_reset(h))
+
+
+def wf_finish_stream(h, n_chunk):
+    _check(_lib.wf_finish_stream(h, n_chunk))
 
 
 def wf_kv_publish(h, plan, layer, q, k, v, q_rot, stream=None):

@@ -29,6 +29,7 @@ class Workload:
     W_store: int = -1
     anchor: int = 1
     q_head_scale: bool = False     # per-head U(0.5, 2) scale on q
+    max_frames: int = 0            # unbounded requests (n_chunk <= 0): frames reachable
 
     @property
     def n_tokens(self) -> int:
@@ -37,7 +38,8 @@ class Workload:
     def config(self) -> "wf.wf_config":
         return wf.make_config(self.S, self.W, self.n_chunk, self.F, self.Hh, self.Ww,
                               self.n_heads, self.head_dim, self.n_layers, W_store=self.W_store,
-                              anchor=self.anchor, dtype=self.dtype, mask=self.mask)
+                              anchor=self.anchor, dtype=self.dtype, mask=self.mask,
+                              max_frames=self.max_frames)
 
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)

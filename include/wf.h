@@ -48,8 +48,12 @@
  *                         page_elems = 2 * H * N * D.
  *   pool                  [L][n_slots] pages, n_slots = 4 + max(W, W_store) + 2 S.
  *   anchor_raw            [L] pages holding chunk 0's unrotated K and its Vt.
- *   tables                fp32 cos/sin pairs written by wf_bind, rounded up to
- *                         256 bytes, then (bf16, FP8, FP8K) the attention's
+ *   tables                written by wf_bind: the frame-axis frequencies
+ *                         theta^(-m/nt) in fp64, then fp32 cos/sin pairs of
+ *                         the row and column axes, rounded up to 256 bytes
+ *                         (the frame-axis angles are computed on the device
+ *                         from the absolute frame, so no table grows with the
+ *                         request), then (bf16, FP8, FP8K) the attention's
  *                         split scratch: 4 x ([N][H][D] + [N][H][2]) fp32,
  *                         the partial results of at most two split groups.
  *
@@ -101,7 +105,8 @@ extern "C" {
 typedef enum {
   WF_OK = 0,
   WF_EINVAL = -1,       /* bad argument, config or pointer                  */
-  WF_ERANGE = -2,       /* round index outside [0, n_chunk + S)             */
+  WF_ERANGE = -2,       /* round index outside [0, n_chunk + S) (unbounded:
+                           F (k + 1) > max_frames)                          */
   WF_EORDER = -3,       /* plan not for this handle / not the next round /
                            attention before publish / commit before publish */
   WF_ESMALL = -4,       /* a caller buffer is smaller than required         */
@@ -142,14 +147,20 @@ typedef struct {
   int32_t W_store;    /* history pages the store reads; -1 = W + S, i.e. the
                          same (W + S + 2)-chunk context budget as stage 0      */
   int32_t anchor;     /* 1 = keep chunk 0 as persistent anchor, 0 = none       */
-  int32_t n_chunk;    /* chunks in the request (>= 1); rounds = n_chunk + S    */
+  int32_t n_chunk;    /* chunks in the request (>= 1); rounds = n_chunk + S.
+                         <= 0: an unbounded request (a stream, WF §1 and
+                         App. B.8): every chunk k >= 0 is admitted in round k,
+                         no drain until wf_finish_stream                      */
   int32_t F, Hh, Ww;  /* latent frames per chunk, token rows, token columns    */
   int32_t n_heads;    /* H                                                    */
   int32_t head_dim;   /* D (even, >= 6)                                       */
   int32_t n_layers;   /* L                                                    */
   int32_t dtype;      /* wf_dtype of q/k/v/q_rot/out and of the pages          */
   int32_t mask;       /* wf_mask                                              */
-  int32_t reserved;   /* must be 0                                            */
+  int32_t max_frames; /* unbounded requests: the latent frames the stream may
+                         reach, in [F, 2^30] (round k needs F (k + 1) <=
+                         max_frames); bounded requests: 0.  No buffer depends
+                         on it: attention storage is the same slot ring.     */
   double rope_theta;  /* RoPE base; 0 selects 10000                            */
   double softmax_scale; /* 0 selects 1/sqrt(head_dim)                          */
 } wf_config;
@@ -220,8 +231,8 @@ typedef struct {
 
 typedef struct wf_handle wf_handle;
 
-/* Text for a status code (static storage). */
-const char* wf_strerror(wf_status status);
+/* Text for a status code (static storage); any int32 is accepted. */
+const char* wf_strerror(int32_t status);
 
 /* Detail of the last failing call on this thread ("" if none). */
 const char* wf_last_error(void);
@@ -256,11 +267,25 @@ wf_status wf_bind(wf_handle* h, void* d_pool, size_t pool_bytes,
                   void* d_tables, size_t table_bytes);
 
 /* Plan round k (host only, no device calls; valid before wf_bind).
- * WF_ERANGE if k is outside [0, n_chunk + S). */
+ * WF_ERANGE if k is outside [0, n_chunk + S), or for an unbounded request if
+ * F (k + 1) > max_frames.  An unbounded request's plan of round k equals the
+ * plan of a bounded request of any n_chunk > k (its config hash aside). */
 wf_status wf_round_plan(const wf_handle* h, int64_t k, wf_plan* out);
 
 /* Round index the handle expects next (0 after create / reset). */
 wf_status wf_next_round(const wf_handle* h, int64_t* k);
+
+/* End an unbounded request (WF §1: the stream stops): it becomes the
+ * bounded request of n_chunk chunks, whose rounds next..n_chunk + S - 1
+ * admit the remaining chunks and drain the pipeline (App. B.3).  n_chunk
+ * must be at least the next round (every chunk admitted so far stays) and
+ * F n_chunk <= 2^30; the handle's config then has n_chunk set and
+ * max_frames 0, so plans of the following rounds are those of that bounded
+ * request, hash included (plans made before the call are rejected).  Call it
+ * between rounds (WF_EORDER once a layer of the next round is published).
+ * Buffers stay bound: their sizes do not depend on n_chunk.  WF_EINVAL for a
+ * bounded handle or an n_chunk out of range.  Host only. */
+wf_status wf_finish_stream(wf_handle* h, int64_t n_chunk);
 
 /* Start a new request at round 0.  Page contents become meaningless. */
 wf_status wf_reset(wf_handle* h);

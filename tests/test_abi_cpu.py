@@ -32,7 +32,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     assert {"wf_dit_workspace_bytes", "wf_dit_layer", "wf_dit_round"} <= set(names)
     lib = ctypes.CDLL(wf.LIB_PATH)
     for n in names:
@@ -84,7 +84,8 @@ def test_pool_bytes():
     page = 2 * 4680 * 12 * 128 * 2
     assert pool == 30 * 20 * page
     assert anc == 30 * page
-    rope = (133 * 3 * 22 + 30 * 21 + 52 * 21) * 8
+    # frame-axis frequencies (22 doubles), then row and column cos/sin tables
+    rope = 22 * 8 + (30 * 21 + 52 * 21) * 8
     nh = 4680 * 12
     # RoPE tables rounded up to 256 bytes, then the split scratch: two split
     # groups x two halves x (O [N][H][D] + (e, l) [N][H]) in fp32
@@ -187,8 +188,10 @@ def test_fp8_unsupported_shapes():
 
 BAD = [dict(S=0), dict(S=9), dict(W=-1), dict(W_store=-2), dict(anchor=2), dict(n_chunk=0),
        dict(F=0), dict(n_heads=0), dict(head_dim=7), dict(head_dim=4), dict(n_layers=0),
-       dict(dtype=5), dict(mask=3), dict(reserved=1), dict(rope_theta=-1.0),
-       dict(rope_theta=0.5), dict(softmax_scale=-1.0), dict(W=40, S=8)]
+       dict(dtype=5), dict(mask=3), dict(max_frames=5), dict(rope_theta=-1.0),
+       dict(rope_theta=0.5), dict(softmax_scale=-1.0), dict(W=40, S=8),
+       dict(n_chunk=0, max_frames=2), dict(n_chunk=-1, max_frames=(1 << 30) + 1),
+       dict(n_chunk=1 << 29)]
 
 
 @pytest.mark.parametrize("bad", BAD, ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
@@ -312,5 +315,93 @@ def test_split_mode_checked_on_the_host():
 def test_fp32_rounds_have_no_split_scratch():
     from chunk_causal_dit_round_amd.workloads import TINY_FP32
     _, _, tab = wf.wf_pool_bytes(TINY_FP32.config())
-    rope = (6 * 3 * 12 + 4 * 10 + 6 * 10) * 8    # 18 frames; 12, 10, 10 pairs of 64 dims
+    # 12 frame-axis frequencies (fp64, padded to 16 bytes); cos/sin of the
+    # 4 rows and 6 columns, 10 pairs each (64 dims: 12, 10, 10 pairs)
+    rope = 12 * 8 + (4 * 10 + 6 * 10) * 8
     assert tab == -(-rope // 256) * 256
+
+
+def _plan_bytes(p):
+    return bytes(memoryview(p))
+
+
+@pytest.mark.parametrize("w", [TINY_FP32, WAN13B_4STEP, WAN13B_4STEP_FP8K], ids=lambda w: w.name)
+def test_unbounded_request_plans(w):
+    """n_chunk <= 0: the plan of every round equals the oracle's unbounded
+    plan, every field of it (hash aside) equals the plan of the bounded
+    request of k + 1 + S chunks, rounds stop where F (k + 1) would exceed
+    max_frames, and no buffer size depends on the request's length."""
+    rounds = 200
+    ub = w.with_(n_chunk=0)
+    cfg = ub.config()
+    cfg.max_frames = w.F * rounds
+    h = wf.wf_create(cfg)
+    oc = oracle_cfg(cfg)
+    assert oc.unbounded
+    try:
+        for k in range(rounds):
+            got = wf.plan_to_dict(wf.wf_round_plan(h, k))
+            want = P.plan(oc, k)
+            for key in ("k", "cells", "groups", "anchor", "evict", "kv_tokens", "n_active"):
+                assert got[key] == want[key], (k, key)
+            assert got["flops"] == want["flops"]
+            if k % 23 == 0:
+                hb = wf.wf_create(w.with_(n_chunk=k + 1 + w.S).config())
+                assert wf.plan_to_dict(wf.wf_round_plan(hb, k)) == got
+                wf.wf_destroy(hb)
+        assert wf.status_of(wf.wf_round_plan, h, rounds) == wf.WF_ERANGE
+        assert "max_frames" in wf.wf_last_error()
+    finally:
+        wf.wf_destroy(h)
+    assert wf.wf_pool_bytes(cfg) == wf.wf_pool_bytes(w.config())
+    a, b = wf.wf_page_layout(cfg), wf.wf_page_layout(w.config())
+    assert all(getattr(a, f) == getattr(b, f) for f, _ in wf.wf_layout._fields_)
+
+
+def test_finish_stream_turns_into_the_bounded_request():
+    """wf_finish_stream(n): the handle's following plans are byte for byte
+    those of a handle created for the bounded request of n chunks (config
+    hash included), fill and drain alike; plans made before are rejected;
+    bounded handles and n out of range are refused."""
+    w = TINY_FP32
+    cfg = w.with_(n_chunk=0).config()
+    cfg.max_frames = 1 << 20
+    h = wf.wf_create(cfg)
+    old = wf.wf_round_plan(h, 0)
+    assert wf.status_of(wf.wf_finish_stream, h, 0) == wf.WF_EINVAL
+    wf.wf_finish_stream(h, 7)
+    hb = wf.wf_create(w.with_(n_chunk=7).config())
+    try:
+        for k in range(7 + w.S):
+            assert _plan_bytes(wf.wf_round_plan(h, k)) == _plan_bytes(wf.wf_round_plan(hb, k))
+        assert wf.status_of(wf.wf_round_plan, h, 7 + w.S) == wf.WF_ERANGE
+        assert old.config_hash != wf.wf_round_plan(h, 0).config_hash
+        assert wf.status_of(wf.wf_finish_stream, h, 9) == wf.WF_EINVAL      # now bounded
+        assert wf.status_of(wf.wf_finish_stream, hb, 9) == wf.WF_EINVAL
+        assert "bounded" in wf.wf_last_error()
+    finally:
+        wf.wf_destroy(h)
+        wf.wf_destroy(hb)
+
+
+def test_device_failure_is_reported_as_wf_edevice():
+    """WF_EDEVICE, forced from the host: with no GPU visible, the table
+    upload of a valid, supported and correctly sized wf_bind fails inside
+    the HIP runtime; the call returns WF_EDEVICE and wf_last_error names the
+    HIP error (the buffer addresses are never dereferenced: no device)."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible: the upload would run")
+    cfg = TINY_FP32.config()
+    h = wf.wf_create(cfg)
+    try:
+        pb, ab, tb = wf.wf_pool_bytes(cfg)
+        fake = 1 << 20
+        assert wf.status_of(wf.wf_bind, h, fake, pb, fake, ab, fake, tb) == wf.WF_EDEVICE
+        err = wf.wf_last_error()
+        assert err.startswith("table upload: ") and len(err) > len("table upload: "), err
+        plan = wf.wf_round_plan(h, 0)
+        # the handle stays unbound: later calls fail before any device work
+        assert wf.status_of(wf.wf_kv_publish, h, plan, 0, fake, fake, fake, fake, 0) == wf.WF_EINVAL
+    finally:
+        wf.wf_destroy(h)

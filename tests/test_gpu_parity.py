@@ -291,6 +291,44 @@ def test_full_size_wan13b_4step_fp8k_sampled():
         ro.close()
 
 
+@pytest.mark.parametrize("dtype", [wf.WF_BF16, wf.WF_FP8], ids=["bf16", "fp8"])
+def test_unbounded_stream_finished_and_drained(dtype):
+    """A stream (n_chunk = 0, WF §1): rounds 0..13 run with no last chunk
+    known, then wf_finish_stream(14) ends it and rounds 14..16 drain.  Every
+    round is checked against the oracle of the 14-chunk request (pages,
+    q_rot, every attention output; the plans of the first 14 rounds are the
+    same), and the outputs equal, bit for bit, those of the same inputs run
+    as a bounded request from the start."""
+    wb = Workload(f"stream_{dtype}", S=3, W=2, n_chunk=14, F=2, Hh=8, Ww=12, n_heads=2,
+                  head_dim=128, n_layers=2, dtype=dtype)
+    wu = wb.with_(n_chunk=0, max_frames=wb.F * 64)
+    rounds = wb.n_chunk + wb.S
+    ref = []
+    rb = Rollout(wb, tag=wb.name)
+    try:
+        for k in range(rounds):
+            rb.run(k)
+            torch.cuda.synchronize()
+            ref.append(rb.sess.bufs["out"].clone())
+    finally:
+        rb.close()
+    ru = Rollout(wu, tag=wb.name)
+    ru.w = wb                       # the oracle's view: the request as it ends
+    worst = 0.0
+    try:
+        for k in range(rounds):
+            if k == wb.n_chunk:
+                wf.wf_finish_stream(ru.sess.h, wb.n_chunk)
+            ru.run(k)
+            for layer in range(wb.n_layers):
+                check_publish(ru, k, layer)
+                worst = max(worst, check_attention(ru, k, layer))
+            assert torch.equal(ru.sess.bufs["out"], ref[k]), f"round {k}: stream != bounded"
+    finally:
+        ru.close()
+    _log(f"  {rounds} rounds, max abs err {worst:.3e}")
+
+
 SPLIT_CASES = [SMALL_BF16[0], SMALL_BF16[1], SMALL_BF16[2], SMALL_BF16[3], SMALL_FP8[0], SMALL_FP8[2],
                SMALL_FP8K[0], SMALL_FP8K[2], SMALL_FP8K[3]]
 
