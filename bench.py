@@ -63,33 +63,39 @@ PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector (plain FMA on the SIMDs)
 CSRC = os.path.join(ROOT, "chunk_causal_dit_round_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
-# Attention instance per page type: peak, dtype label, kernel, its source, the
-# committed counter summary its HBM traffic comes from and the workload the
-# counters were taken on.
+# Attention instance per page type: peak, dtype label, kernel and its source.
 PAGE_KINDS = {
     "bf16": dict(peak=PEAK_BF16_TFLOPS, dtype="bf16", kernel="wf_attention_bf16_kernel<128>",
-                 src="wf_attention.hip", traffic="attention_bf16_wan1.3b_4step_hbm_traffic.txt",
-                 workload="wan1.3b_4step", what="bf16 MFMA peak"),
+                 src="wf_attention.hip", what="bf16 MFMA peak"),
     "fp8": dict(peak=PEAK_FP8_TFLOPS, dtype="fp8", kernel="wf_attention_fp8_kernel",
-                src="wf_attention_fp8.hip",
-                traffic="attention_fp8_wan1.3b_4step_kernel_trace_and_traffic.txt",
-                workload="wan1.3b_4step_fp8", what="fp8 MFMA peak (FP8 E4M3 pages)"),
+                src="wf_attention_fp8.hip", what="fp8 MFMA peak (FP8 E4M3 pages)"),
     "fp8k": dict(peak=PEAK_FP8K_TFLOPS, dtype="fp8 QK^T + bf16 PV", kernel="wf_attention_fp8k_kernel",
                  src="wf_attention_fp8k.hip",
-                 traffic="attention_fp8k_wan1.3b_4step_kernel_trace_and_traffic.txt",
-                 workload="wan1.3b_4step_fp8k", what="blended fp8 / bf16 MFMA peak (8-bit-key pages: FP8 K, bf16 V)"),
+                 what="blended fp8 / bf16 MFMA peak (8-bit-key pages: FP8 K, bf16 V)"),
+}
+
+# The committed counter summary (profiles/) that each workload's attention
+# traffic comes from: FETCH_SIZE + WRITE_SIZE per launch, scaled by a device
+# copy of known size.
+TRAFFIC_FILES = {
+    "wan1.3b_4step": "attention_bf16_wan1.3b_4step_hbm_traffic.txt",
+    "wan1.3b_4step_fp8": "attention_fp8_wan1.3b_4step_kernel_trace_and_traffic.txt",
+    "wan1.3b_4step_fp8k": "attention_fp8k_wan1.3b_4step_kernel_trace_and_traffic.txt",
+    "wan1.3b_5step": "attention_bf16_wan1.3b_5step_kernel_trace_and_traffic.txt",
+    "wan1.3b_5step_rolling": "attention_bf16_wan1.3b_5step_rolling_kernel_trace_and_traffic.txt",
+    "wan14b_4step": "attention_bf16_wan14b_4step_kernel_trace_and_traffic.txt",
 }
 
 
 def measured_traffic(kind, workload):
-    """HBM bytes per attention launch from the committed counter summary, or
-    None if the kernel source changed since the counters were taken or the
-    counters were taken on another workload."""
-    if workload != kind["workload"]:
+    """HBM bytes per attention launch from the workload's committed counter
+    summary, or None if there is none or the kernel source changed since
+    the counters were taken."""
+    name = TRAFFIC_FILES.get(workload)
+    if name is None:
         return None
     try:
-        fields = dict(line.split(":", 1) for line in open(os.path.join(PROFILES, kind["traffic"]))
-                      if ":" in line)
+        fields = dict(line.split(":", 1) for line in open(os.path.join(PROFILES, name)) if ":" in line)
         src = hashlib.sha256(open(os.path.join(CSRC, kind["src"]), "rb").read()).hexdigest()
         if fields.get("kernel_source_sha256", "").strip() != src:
             return None
