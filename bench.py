@@ -371,6 +371,7 @@ def dit_rollout(args, w):
     ffn = args.ffn or (13824 if w.n_heads == 40 else 8960)
     sess = Session(w.config(), device=dev, io=False)
     ds = DitSession(sess, ffn, tag="rollout-dit")
+    ds.tune()                        # fastest hipBLASLt algorithm per product (blocking, untimed)
     n_rounds = w.n_chunk + w.S
     w_store = w.W + w.S if w.W_store < 0 else w.W_store
     k_steady = w.S + max(w.W, w_store) + 1
@@ -424,6 +425,7 @@ def dit_bench(args, w):
         ds.load_x0(i)
         x_sets.append(ds.x.clone())
     stream = torch.cuda.current_stream()
+    ds.tune(stream)                  # fastest hipBLASLt algorithm per product (blocking, untimed)
 
     def run(k):
         ds.x.copy_(x_sets[k % 2])

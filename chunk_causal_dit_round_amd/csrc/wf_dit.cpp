@@ -30,6 +30,7 @@ struct Gemm {
   hipblasLtMatmulDesc_t desc = nullptr;
   hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, ld = nullptr;
   hipblasLtMatmulAlgo_t algo;
+  bool tuned = false;
 };
 
 struct DitState {
@@ -174,6 +175,59 @@ wf_status gemm(DitState* d, int m, int n, int k, hipDataType out, hipblasLtEpilo
   return ok();
 }
 
+// Times the heuristic's first candidates for one product shape on the given
+// operands (2 warm-up and 5 timed runs each, HIP events on `st`) and keeps
+// the fastest.  Candidates the library rejects at run time are skipped.
+wf_status tune_gemm(DitState* d, int m, int n, int k, hipDataType out, hipblasLtEpilogue_t epi, const void* W,
+                    const void* B, void* D, const void* bias, void* ws, hipStream_t st) {
+  Gemm* g = nullptr;
+  wf_status r = gemm_plan(d, m, n, k, out, epi, &g);
+  if (r != WF_OK || g->tuned) return r;
+  hipblasLtMatmulPreference_t pref = nullptr;
+  hipblasStatus_t s = hipblasLtMatmulPreferenceCreate(&pref);
+  const uint64_t wsb = kLtWorkspace;
+  if (s == HIPBLAS_STATUS_SUCCESS)
+    s = hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &wsb, sizeof(wsb));
+  hipblasLtMatmulHeuristicResult_t hr[WF_DIT_TUNE_CANDIDATES];
+  int n_res = 0;
+  if (s == HIPBLAS_STATUS_SUCCESS)
+    s = hipblasLtMatmulAlgoGetHeuristic(d->lt, g->desc, g->la, g->lb, g->ld, g->ld, pref, WF_DIT_TUNE_CANDIDATES,
+                                        hr, &n_res);
+  if (pref) hipblasLtMatmulPreferenceDestroy(pref);
+  if (s != HIPBLAS_STATUS_SUCCESS) return fail(WF_EDEVICE, lt_error("hipBLASLt heuristic", s));
+  s = hipblasLtMatmulDescSetAttribute(g->desc, HIPBLASLT_MATMUL_DESC_BIAS_POINTER, &bias, sizeof(bias));
+  if (s != HIPBLAS_STATUS_SUCCESS) return fail(WF_EDEVICE, lt_error("hipBLASLt bias", s));
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+    if (e0) (void)hipEventDestroy(e0);
+    return fail(WF_EDEVICE, "hipEventCreate failed");
+  }
+  const float alpha = 1.f, beta = 0.f;
+  float best_ms = 0.f;
+  int best = -1;
+  for (int i = 0; i < n_res; ++i) {
+    auto run = [&]() {
+      return hipblasLtMatmul(d->lt, g->desc, &alpha, W, g->la, B, g->lb, &beta, D, g->ld, D, g->ld, &hr[i].algo,
+                             ws, kLtWorkspace, st);
+    };
+    if (run() != HIPBLAS_STATUS_SUCCESS || run() != HIPBLAS_STATUS_SUCCESS) continue;
+    bool ok_run = hipEventRecord(e0, st) == hipSuccess;
+    for (int rep = 0; rep < 5 && ok_run; ++rep) ok_run = run() == HIPBLAS_STATUS_SUCCESS;
+    float ms = 0.f;
+    ok_run = ok_run && hipEventRecord(e1, st) == hipSuccess && hipEventSynchronize(e1) == hipSuccess &&
+             hipEventElapsedTime(&ms, e0, e1) == hipSuccess;
+    if (ok_run && (best < 0 || ms < best_ms)) {
+      best = i;
+      best_ms = ms;
+    }
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (best >= 0) g->algo = hr[best].algo;
+  g->tuned = true;
+  return ok();
+}
+
 wf_status kernel_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(WF_EDEVICE, std::string(what) + ": " + hipGetErrorString(e));
   return ok();
@@ -313,6 +367,34 @@ wf_status wf_dit_layer(wf_handle* h, const wf_plan* plan, int32_t layer, const w
   if ((s = wf::check_call(h, dc, w, 1, d_mod, d_x, d_work, work_bytes)) != WF_OK) return s;
   return wf::dit_layer(h, p, layer, *dc, *w, static_cast<const float*>(d_mod), static_cast<float*>(d_x),
                        static_cast<char*>(d_work), static_cast<hipStream_t>(stream));
+}
+
+wf_status wf_dit_tune(wf_handle* h, const wf_dit_config* dc, const wf_dit_weights* w, void* d_work,
+                      size_t work_bytes, void* stream) {
+  if (!h) return fail(WF_EINVAL, "handle is NULL");
+  if (!h->bound) return fail(WF_EINVAL, "handle is not bound (call wf_bind first)");
+  // the block's checks with the work buffer standing in for mod and x
+  wf_status s = wf::check_call(h, dc, w, 1, d_work, d_work, d_work, work_bytes);
+  if (s != WF_OK) return s;
+  const wf::Shape& sh = h->sh;
+  const int rows = (sh.S + 1) * sh.N, C = sh.H * sh.D, F = dc->ffn_dim;
+  const wf::Layout L = wf::layout_of(sh, F);
+  char* work = static_cast<char*>(d_work);
+  void* ws = work + L.lt;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  wf::DitState* d = h->dit;
+  s = wf::tune_gemm(d, 3 * C, rows, C, HIP_R_16BF, HIPBLASLT_EPILOGUE_BIAS, w->w_qkv, work + L.h, work + L.qkv,
+                    w->b_qkv, ws, st);
+  if (s == WF_OK)
+    s = wf::tune_gemm(d, C, rows, C, HIP_R_32F, HIPBLASLT_EPILOGUE_BIAS, w->w_o, work + L.o, work + L.y, w->b_o,
+                      ws, st);
+  if (s == WF_OK)
+    s = wf::tune_gemm(d, F, rows, C, HIP_R_16BF, HIPBLASLT_EPILOGUE_GELU_BIAS, w->w_1, work + L.h, work + L.f,
+                      w->b_1, ws, st);
+  if (s == WF_OK)
+    s = wf::tune_gemm(d, C, rows, F, HIP_R_32F, HIPBLASLT_EPILOGUE_BIAS, w->w_2, work + L.f, work + L.y, w->b_2,
+                      ws, st);
+  return s;
 }
 
 wf_status wf_dit_round(wf_handle* h, const wf_plan* plan, const wf_dit_config* dc, const wf_dit_weights* w,

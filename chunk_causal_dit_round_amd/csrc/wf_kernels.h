@@ -94,10 +94,11 @@ constexpr int kAttnBM_f32 = 64;
 // FP8 / FP8K attention keeps the scale codes of a group's whole context in LDS.
 constexpr int kFp8MaxCtxTiles = 4096;
 
-// The publish kernels compute the frame-axis cos/sin of a 64-token block in
-// LDS: at most 64 frames x the frame axis's pairs (22 for head_dim <= 128).
-constexpr int kMaxFramePairs = 22;
-constexpr int kMaxFrameEntries = 64 * kMaxFramePairs;
+// The publish kernels stage a 64-token block's rotation angles in LDS: the
+// cos/sin of every (token, pair) of the block, and the frame axis's at the
+// frames the block spans.  Bytes of those tables, and the most allowed.
+size_t publish_lds_bytes(int F, int Hh, int Ww, int D, int nt);
+constexpr size_t kPublishMaxLds = 60 * 1024;
 
 hipError_t launch_publish(const PublishArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_attention(const AttnArgs& a, int dtype, hipStream_t stream);

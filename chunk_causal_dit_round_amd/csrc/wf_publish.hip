@@ -8,20 +8,21 @@
 // the window shifts (TASK_CAPTURE / TASK_ANCHOR).
 //
 // Grid: (64-token blocks, head groups, tasks).  A work-group owns one block
-// of 64 tokens of one task and a group of heads, which it walks a few heads
-// at a time.  A thread owns 8 consecutive tokens x one 16-byte chunk of a
+// of 64 tokens of one task and the heads one pass of its threads covers (two
+// at D = 128).  A thread owns 8 consecutive tokens x one 16-byte chunk of a
 // head row (8 bf16 / 4 fp32 elements):
-//   * its rotation angles depend on the token and the pair, not on the head,
-//     so the thread forms its cos/sin once and reuses them for every head of
-//     the group;
-//   * the frame-axis cos/sin come from the absolute frame position, computed
-//     in fp64 per work-group (frames x pairs of the block), so positions are
-//     not bounded by the length of a table; the row and column tables are
-//     fixed (Hh and Ww positions);
-//   * the thread's 8 x 8 (bf16) block of V is transposed in registers, so the
-//     page's Vt rows (keys contiguous) are written with 16-byte stores; eight
-//     consecutive lanes own the 8 token groups of one chunk, which makes every
-//     load and store a 128-byte contiguous segment.
+//   * the rotation angles depend on the token and the pair, not on the head:
+//     the work-group stages the cos/sin of every (token, pair) of its block
+//     in LDS once, for all its heads; the frame axis's come from the absolute
+//     frame position, computed in fp64 (so positions are not bounded by the
+//     length of a table), the row and column axes' from fixed tables;
+//   * a thread issues all 24 row loads of a head (q, k, v) before it uses
+//     any, with no branch between them (the rows of a token group are valid
+//     together: N % 8 == 0 for bf16, FP8 and FP8K; fp32 clamps its rows);
+//   * its 8 x 8 (bf16) block of V is transposed in registers, so the page's
+//     Vt rows (keys contiguous) are written with 16-byte stores; eight
+//     consecutive lanes own the 8 token groups of one chunk, which makes
+//     every load and store a 128-byte contiguous segment.
 // HBM-bound: every byte is read once and written once.
 #include <hip/hip_runtime.h>
 
@@ -70,62 +71,67 @@ __device__ inline Geom geom(int D, int vec) {
   return q;
 }
 
-// cos/sin of the frame-axis pairs at every frame the block's tokens span:
-// angle = (frame0 + f) * omega_m in fp64, rounded to fp32.  ftab[f * nt + m].
-__device__ inline int frame_table(const PublishArgs& a, int frame0, int tok0, float2* ftab) {
+// Angle tables of the work-group in LDS (float2 cos/sin):
+//   ctab [64][P]    every (token of the block, pair): the thread reads its
+//                   token's VEC / 2 consecutive pairs with immediate offsets
+//   ftab [frames_max][nt] the frame axis at the frames the block spans,
+//                   computed in fp64 from the absolute frame position (so
+//                   positions are not bounded by a table's length)
+// The row and column axes come from the fixed rope_hw tables.
+__device__ inline void stage_angles(const PublishArgs& a, int frame0, int tok0, float2* ctab,
+                                    float2* ftab) {
   const int hw = a.Hh * a.Ww;
   const int last = min(tok0 + kTokens, a.N) - 1;
   const int f_lo = tok0 / hw;
-  const int n = (last / hw - f_lo + 1) * a.nt;
-  for (int i = threadIdx.x; i < n; i += kThreads) {
+  const int nf = (last / hw - f_lo + 1) * a.nt;
+  for (int i = threadIdx.x; i < nf; i += kThreads) {
     const int f = i / a.nt, m = i - f * a.nt;
     const double ang = static_cast<double>(static_cast<int64_t>(frame0) + f_lo + f) * a.omega_t[m];
     double s, c;
     sincos(ang, &s, &c);
     ftab[i] = make_float2(static_cast<float>(c), static_cast<float>(s));
   }
-  return f_lo;
-}
-
-// cos/sin of this thread's pairs (VEC / 2 per token) for its 8 tokens.
-template <int VEC>
-__device__ inline void thread_angles(const PublishArgs& a, const float2* ftab, int f_lo, int t0,
-                                     int c, float2 (&cs)[kRows][VEC / 2]) {
-  const float2* th = a.rope_hw;              // [Hh][nh]
-  const float2* tw = th + a.Hh * a.nh;       // [Ww][nw]
-  const int hw = a.Hh * a.Ww;
-#pragma unroll
-  for (int i = 0; i < kRows; ++i) {
-    const int tok = min(t0 + i, a.N - 1);    // rows past N are never stored
+  __syncthreads();
+  // Four threads per token: one token's position is decoded once, then each
+  // thread fills every fourth pair of the token's row.
+  const int P = a.D / 2;
+  static_assert(kThreads == 4 * kTokens, "four threads per token");
+  {
+    const int r = threadIdx.x >> 2, p0 = threadIdx.x & 3;
+    const int tok = min(tok0 + r, a.N - 1);                    // rows past N are never stored
     const int f = tok / hw - f_lo, y = (tok / a.Ww) % a.Hh, x = tok % a.Ww;
-#pragma unroll
-    for (int e = 0; e < VEC / 2; ++e) {
-      const int p = (c * VEC >> 1) + e;
+    const float2* fr = ftab + f * a.nt;                        // LDS
+    const float2* yr = a.rope_hw + y * a.nh - a.nt;            // row table [Hh][nh]
+    const float2* xr = a.rope_hw + a.Hh * a.nh + x * a.nw - (a.nt + a.nh);   // column table
+    float2* out = ctab + r * P;
+    for (int p = p0; p < P; p += 4) {
       if (p < a.nt) {
-        cs[i][e] = ftab[f * a.nt + p];
+        out[p] = fr[p];
       } else if (p < a.nt + a.nh) {
-        cs[i][e] = th[y * a.nh + (p - a.nt)];
+        out[p] = yr[p];
       } else {
-        cs[i][e] = tw[x * a.nw + (p - a.nt - a.nh)];
+        out[p] = xr[p];
       }
     }
   }
+  __syncthreads();
 }
 
-// Rotated pairs (x_2e, x_2e+1) -> (x0 cos - x1 sin, x0 sin + x1 cos), fp32.
+// Rotated pairs (x_2e, x_2e+1) -> (x0 cos - x1 sin, x0 sin + x1 cos), fp32;
+// cs = the row's VEC / 2 consecutive (cos, sin) pairs.
 template <int VEC, typename R>
-__device__ inline void rotate_f32(const R& x, const float2 (&cs)[VEC / 2], float (&out)[VEC]) {
+__device__ inline void rotate_f32(const R& x, const float2* cs, float (&out)[VEC]) {
 #pragma unroll
   for (int e = 0; e < VEC / 2; ++e) {
+    const float2 w = cs[e];
     const float x0 = static_cast<float>(x[2 * e]), x1 = static_cast<float>(x[2 * e + 1]);
-    out[2 * e] = x0 * cs[e].x - x1 * cs[e].y;
-    out[2 * e + 1] = x0 * cs[e].y + x1 * cs[e].x;
+    out[2 * e] = x0 * w.x - x1 * w.y;
+    out[2 * e + 1] = x0 * w.y + x1 * w.x;
   }
 }
 
 template <typename T>
-__device__ inline typename Vec<T>::raw rotate(const typename Vec<T>::raw& x,
-                                              const float2 (&cs)[Vec<T>::n / 2]) {
+__device__ inline typename Vec<T>::raw rotate(const typename Vec<T>::raw& x, const float2* cs) {
   constexpr int VEC = Vec<T>::n;
   float r[VEC];
   rotate_f32<VEC>(x, cs, r);
@@ -135,80 +141,87 @@ __device__ inline typename Vec<T>::raw rotate(const typename Vec<T>::raw& x,
   return out;
 }
 
+// 16-byte access at a 32-bit byte offset from a uniform base (one layer's
+// tensors and slots stay below 4 GiB, checked on the host).
+template <typename R>
+__device__ inline R ld16(const void* base, uint32_t off) {
+  return *reinterpret_cast<const R*>(static_cast<const char*>(base) + off);
+}
+template <typename R>
+__device__ inline void st16(void* base, uint32_t off, const R& v) {
+  *reinterpret_cast<R*>(static_cast<char*>(base) + off) = v;
+}
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void wf_publish_kernel(const PublishArgs a) {
   using raw = typename Vec<T>::raw;
   constexpr int VEC = Vec<T>::n;
   constexpr int kPieces = kRows / VEC;          // 16-byte pieces of 8 tokens
-  __shared__ float2 ftab[kMaxFrameEntries];
+  constexpr uint32_t E = sizeof(T);
+  extern __shared__ float2 lds_tab[];
 
   const PublishTask task = a.task[blockIdx.z];
   const int tok0 = blockIdx.x * kTokens;
   const int hg0 = blockIdx.y * a.heads_per_group;
   const int hg1 = min(a.H, hg0 + a.heads_per_group);
-  const int N = a.N, H = a.H, D = a.D;
+  const int N = a.N, H = a.H, D = a.D, P = D / 2;
+  float2* ctab = lds_tab;
+  stage_angles(a, task.frame0, tok0, ctab, lds_tab + kTokens * P);
   const Geom q = geom(D, VEC);
-  const int f_lo = frame_table(a, task.frame0, tok0, ftab);
-  __syncthreads();
-  if (q.slot >= q.hpp) return;
-  float2 cs[kRows][VEC / 2];
   const int t0 = tok0 + kRows * q.g;
-  thread_angles<VEC>(a, ftab, f_lo, t0, q.c, cs);
+  // Rows of the group are valid together (bf16: N % 8 == 0) or, for fp32
+  // (N % 4 == 0), the first four alone; loads clamp to row N - 1.
+  if (q.slot >= q.hpp || t0 >= N) return;
+  const bool full = t0 + kRows <= N;
+  const float2* cs0 = ctab + (kRows * q.g) * P + (VEC / 2) * q.c;   // row i: cs0 + i P
+  uint32_t row[kRows];
+#pragma unroll
+  for (int i = 0; i < kRows; ++i) row[i] = static_cast<uint32_t>(min(i, N - 1 - t0));
 
-  const int64_t hnd = static_cast<int64_t>(H) * N * D;
-  T* pageK = static_cast<T*>(a.pool) + static_cast<int64_t>(task.slot) * a.page_elems;  // [H][N][D]
-  T* pageVt = pageK + hnd;                                                             // [H][D][N]
-  T* ancK = static_cast<T*>(a.anchor_raw);
-  T* ancVt = ancK + hnd;
+  char* slot = static_cast<char*>(a.pool) + static_cast<int64_t>(task.slot) * a.page_bytes;
+  const uint32_t vt_part = static_cast<uint32_t>(H) * N * D * E;   // Vt after K, in a page
   const bool capture = task.mode == TASK_CAPTURE;
+  const uint32_t in_step = static_cast<uint32_t>(H) * D * E;       // one token row of q/k/v
 
   for (int h = hg0 + q.slot; h < hg1; h += q.hpp) {
-    const int64_t krow = (static_cast<int64_t>(h) * N + t0) * D + VEC * q.c;   // K[h][t0][VEC c]
-    const int64_t vrow = (static_cast<int64_t>(h) * D + VEC * q.c) * N + t0;   // Vt[h][VEC c][t0]
+    const uint32_t krow = ((static_cast<uint32_t>(h) * N + t0) * D + VEC * q.c) * E;   // K[h][t0][VEC c]
+    const uint32_t vrow = vt_part + ((static_cast<uint32_t>(h) * D + VEC * q.c) * N + t0) * E;
+    const uint32_t kstep = static_cast<uint32_t>(D) * E, vstep = static_cast<uint32_t>(N) * E;
     if (task.mode == TASK_ANCHOR) {
-      // Key: the kept raw key re-rotated at the anchor's current position.
+      // Key: the kept raw key re-rotated at the anchor's current position;
+      // value: the kept Vt rows copied unchanged.
+      raw xk[kRows], xv[VEC][kPieces];
 #pragma unroll
-      for (int i = 0; i < kRows; ++i) {
-        if (t0 + i >= N) break;
-        const raw x = *reinterpret_cast<const raw*>(ancK + krow + int64_t(i) * D);
-        *reinterpret_cast<raw*>(pageK + krow + int64_t(i) * D) = rotate<T>(x, cs[i]);
-      }
-      // Value: the kept Vt rows copied unchanged.
+      for (int i = 0; i < kRows; ++i) xk[i] = ld16<raw>(a.anchor_raw, krow + row[i] * kstep);
 #pragma unroll
       for (int e = 0; e < VEC; ++e)
 #pragma unroll
-        for (int j = 0; j < kPieces; ++j) {
-          if (t0 + VEC * j >= N) break;
-          const int64_t off = vrow + int64_t(e) * N + VEC * j;
-          *reinterpret_cast<raw*>(pageVt + off) = *reinterpret_cast<const raw*>(ancVt + off);
-        }
+        for (int j = 0; j < kPieces; ++j)
+          xv[e][j] = ld16<raw>(a.anchor_raw, vrow + e * vstep + (full ? VEC * j * E : 0u));
+#pragma unroll
+      for (int i = 0; i < kRows; ++i)
+        if (full || i < VEC) st16(slot, krow + i * kstep, rotate<T>(xk[i], cs0 + i * P));
+#pragma unroll
+      for (int e = 0; e < VEC; ++e)
+#pragma unroll
+        for (int j = 0; j < kPieces; ++j)
+          if (full || j == 0) st16(slot, vrow + e * vstep + VEC * j * E, xv[e][j]);
       continue;
     }
-    const T* qin = static_cast<const T*>(a.q);
-    const T* kin = static_cast<const T*>(a.k);
-    const T* vin = static_cast<const T*>(a.v);
-    T* qr = static_cast<T*>(a.q_rot);
-    const int64_t in0 = ((static_cast<int64_t>(task.stage) * N + t0) * H + h) * D + VEC * q.c;
-    const int64_t in_step = static_cast<int64_t>(H) * D;
+    const uint32_t in0 = (((static_cast<uint32_t>(task.stage) * N + t0) * H + h) * D + VEC * q.c) * E;
     raw xq[kRows], xk[kRows], xv[kRows];
 #pragma unroll
     for (int i = 0; i < kRows; ++i) {
-      if (t0 + i < N) {
-        xq[i] = *reinterpret_cast<const raw*>(qin + in0 + i * in_step);
-        xk[i] = *reinterpret_cast<const raw*>(kin + in0 + i * in_step);
-        xv[i] = *reinterpret_cast<const raw*>(vin + in0 + i * in_step);
-      } else {
-        xq[i] = raw{};
-        xk[i] = raw{};
-        xv[i] = raw{};
-      }
+      xq[i] = ld16<raw>(a.q, in0 + row[i] * in_step);
+      xk[i] = ld16<raw>(a.k, in0 + row[i] * in_step);
+      xv[i] = ld16<raw>(a.v, in0 + row[i] * in_step);
     }
 #pragma unroll
     for (int i = 0; i < kRows; ++i) {
-      if (t0 + i >= N) break;
-      *reinterpret_cast<raw*>(qr + in0 + i * in_step) = rotate<T>(xq[i], cs[i]);
-      *reinterpret_cast<raw*>(pageK + krow + int64_t(i) * D) = rotate<T>(xk[i], cs[i]);
-      if (capture) *reinterpret_cast<raw*>(ancK + krow + int64_t(i) * D) = xk[i];
+      if (!full && i >= VEC) break;             // fp32: the last four rows past N
+      st16(a.q_rot, in0 + i * in_step, rotate<T>(xq[i], cs0 + i * P));
+      st16(slot, krow + i * kstep, rotate<T>(xk[i], cs0 + i * P));
+      if (capture) st16(a.anchor_raw, krow + i * kstep, xk[i]);
     }
     // Transposed write: element e of the chunk is value dim VEC c + e; its
     // 8 tokens go out as kPieces 16-byte pieces.
@@ -216,13 +229,13 @@ __global__ __launch_bounds__(kThreads) void wf_publish_kernel(const PublishArgs 
     for (int e = 0; e < VEC; ++e)
 #pragma unroll
       for (int j = 0; j < kPieces; ++j) {
-        if (t0 + VEC * j >= N) break;
+        if (!full && j > 0) break;
         raw o;
 #pragma unroll
         for (int u = 0; u < VEC; ++u) o[u] = xv[VEC * j + u][e];
-        const int64_t off = vrow + int64_t(e) * N + VEC * j;
-        *reinterpret_cast<raw*>(pageVt + off) = o;
-        if (capture) *reinterpret_cast<raw*>(ancVt + off) = o;
+        const uint32_t off = vrow + e * vstep + VEC * j * E;
+        st16(slot, off, o);
+        if (capture) st16(a.anchor_raw, off, o);
       }
   }
 }
@@ -265,8 +278,8 @@ __device__ inline float wave_max(float v) {
 
 template <bool kBf16V>
 __global__ __launch_bounds__(kThreads) void wf_publish_fp8_kernel(const PublishArgs a) {
-  constexpr int D = kFp8D;
-  __shared__ float2 ftab[kMaxFrameEntries];
+  constexpr int D = kFp8D, P = kFp8D / 2;
+  extern __shared__ float2 lds_tab[];
   __shared__ float red[kThreads / 64][2];
 
   const PublishTask task = a.task[blockIdx.z];
@@ -275,90 +288,64 @@ __global__ __launch_bounds__(kThreads) void wf_publish_fp8_kernel(const PublishA
   const int hg0 = blockIdx.y * a.heads_per_group;
   const int hg1 = min(a.H, hg0 + a.heads_per_group);
   const int N = a.N, H = a.H, Np = a.Npad;
+  float2* ctab = lds_tab;
+  stage_angles(a, task.frame0, tok0, ctab, lds_tab + kTokens * P);
   const Geom q = geom(D, 8);                    // two heads per pass, 2 waves each
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int f_lo = frame_table(a, task.frame0, tok0, ftab);
-  __syncthreads();
-  float2 cs[kRows][4];
   const int t0 = tok0 + kRows * q.g;
-  thread_angles<8>(a, ftab, f_lo, t0, q.c, cs);
+  const bool valid = t0 < N;                    // N % 8 == 0: all 8 rows or none
+  const float2* cs0 = ctab + (kRows * q.g) * P + 4 * q.c;
 
-  uint8_t* page = static_cast<uint8_t*>(a.pool) + static_cast<int64_t>(task.slot) * a.page_bytes;
-  uint8_t* K8 = page;                                                      // [H][Np][D]
-  uint8_t* V8 = page + static_cast<int64_t>(H) * Np * D;                   // [H][D][Np]
-  uint8_t* codes = page + (kBf16V ? 3 : 2) * static_cast<int64_t>(H) * Np * D;   // [H][T][2]
-  const int64_t hnd = static_cast<int64_t>(H) * N * D;
-  __bf16* ancK = static_cast<__bf16*>(a.anchor_raw);                       // bf16 [H][N][D]
-  __bf16* ancVt = ancK + hnd;                                              // bf16 [H][D][N]
+  char* page = static_cast<char*>(a.pool) + static_cast<int64_t>(task.slot) * a.page_bytes;
+  const uint32_t v8_part = static_cast<uint32_t>(H) * Np * D;          // Vt after K8
+  const uint32_t code_part = (kBf16V ? 3u : 2u) * static_cast<uint32_t>(H) * Np * D;
+  const uint32_t anc_vt = static_cast<uint32_t>(H) * N * D * 2u;       // raw Vt after raw K (bf16)
+  const uint32_t in_step = static_cast<uint32_t>(H) * D * 2u;
   const bool capture = task.mode == TASK_CAPTURE;
   const bool anchor = task.mode == TASK_ANCHOR;
 
   for (int hb = hg0; hb < hg1; hb += q.hpp) {   // uniform over the work-group
     const int h = hb + q.slot;
     const bool act = h < hg1;
-    float kr[kRows][8];                         // rotated keys (0 past N)
+    float kr[kRows][8];                         // rotated keys (+0 on padding rows)
     bf16x8 vt[8];                               // values, dim-major: vt[e][i] = v(t0 + i, 8 c + e)
-    float kmax = 0.f, vmax = 0.f;
-    const int64_t krow = (static_cast<int64_t>(h) * N + t0) * D + 8 * q.c;
-    const int64_t vrow = (static_cast<int64_t>(h) * D + 8 * q.c) * N + t0;
-    if (act && anchor) {
 #pragma unroll
-      for (int i = 0; i < kRows; ++i) {
-        if (t0 + i < N) {
-          const bf16x8 x = *reinterpret_cast<const bf16x8*>(ancK + krow + int64_t(i) * D);
-          rotate_f32<8>(x, cs[i], kr[i]);
-        } else {
+    for (int i = 0; i < kRows; ++i)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) kr[i][e] = 0.f;   // padding: +0 codes (a rotated 0 may be -0)
-        }
-      }
+      for (int e = 0; e < 8; ++e) kr[i][e] = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        vt[e] = bf16x8{};
-        if (t0 < N) vt[e] = *reinterpret_cast<const bf16x8*>(ancVt + vrow + int64_t(e) * N);
-      }
-    } else if (act) {
-      const __bf16* qin = static_cast<const __bf16*>(a.q);
-      const __bf16* kin = static_cast<const __bf16*>(a.k);
-      const __bf16* vin = static_cast<const __bf16*>(a.v);
-      __bf16* qr = static_cast<__bf16*>(a.q_rot);
-      const int64_t in0 = ((static_cast<int64_t>(task.stage) * N + t0) * H + h) * D + 8 * q.c;
-      const int64_t in_step = static_cast<int64_t>(H) * D;
+    for (int e = 0; e < 8; ++e) vt[e] = bf16x8{};
+    const uint32_t krow = ((static_cast<uint32_t>(h) * N + t0) * D + 8 * q.c) * 2u;   // raw K (bf16)
+    const uint32_t vrow = anc_vt + ((static_cast<uint32_t>(h) * D + 8 * q.c) * N + t0) * 2u;
+    if (act && valid && anchor) {
+      bf16x8 xk[kRows];
+#pragma unroll
+      for (int i = 0; i < kRows; ++i) xk[i] = ld16<bf16x8>(a.anchor_raw, krow + i * D * 2u);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vt[e] = ld16<bf16x8>(a.anchor_raw, vrow + e * N * 2u);
+#pragma unroll
+      for (int i = 0; i < kRows; ++i) rotate_f32<8>(xk[i], cs0 + i * P, kr[i]);
+    } else if (act && valid) {
+      const uint32_t in0 = (((static_cast<uint32_t>(task.stage) * N + t0) * H + h) * D + 8 * q.c) * 2u;
       bf16x8 xq[kRows], xk[kRows], xv[kRows];
 #pragma unroll
       for (int i = 0; i < kRows; ++i) {
-        xq[i] = bf16x8{};
-        xk[i] = bf16x8{};
-        xv[i] = bf16x8{};
-        if (t0 + i < N) {
-          xq[i] = *reinterpret_cast<const bf16x8*>(qin + in0 + i * in_step);
-          xk[i] = *reinterpret_cast<const bf16x8*>(kin + in0 + i * in_step);
-          xv[i] = *reinterpret_cast<const bf16x8*>(vin + in0 + i * in_step);
-        }
+        xq[i] = ld16<bf16x8>(a.q, in0 + i * in_step);
+        xk[i] = ld16<bf16x8>(a.k, in0 + i * in_step);
+        xv[i] = ld16<bf16x8>(a.v, in0 + i * in_step);
       }
 #pragma unroll
       for (int i = 0; i < kRows; ++i) {
-        if (t0 + i < N) {
-          rotate_f32<8>(xk[i], cs[i], kr[i]);
-          *reinterpret_cast<bf16x8*>(qr + in0 + i * in_step) = rotate<__bf16>(xq[i], cs[i]);
-          if (capture) *reinterpret_cast<bf16x8*>(ancK + krow + int64_t(i) * D) = xk[i];
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) kr[i][e] = 0.f;   // padding: +0 codes (a rotated 0 may be -0)
-        }
+        st16(a.q_rot, in0 + i * in_step, rotate<__bf16>(xq[i], cs0 + i * P));
+        rotate_f32<8>(xk[i], cs0 + i * P, kr[i]);
+        if (capture) st16(a.anchor_raw, krow + i * D * 2u, xk[i]);
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e)
 #pragma unroll
         for (int i = 0; i < kRows; ++i) vt[e][i] = xv[i][e];
-    } else {
-#pragma unroll
-      for (int i = 0; i < kRows; ++i)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) kr[i][e] = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) vt[e] = bf16x8{};
     }
+    float kmax = 0.f, vmax = 0.f;
 #pragma unroll
     for (int i = 0; i < kRows; ++i)
 #pragma unroll
@@ -380,73 +367,76 @@ __global__ __launch_bounds__(kThreads) void wf_publish_fp8_kernel(const PublishA
     if (act) {
       const int ek = fp8_exponent(kmax), ev = kBf16V ? 0 : fp8_exponent(vmax);
       const float sk = ldexpf(1.f, -ek), sv = ldexpf(1.f, -ev);
-      // K rows (padding rows get zero codes)
+      // K rows (padding rows get +0 codes)
+      const uint32_t k8row = (static_cast<uint32_t>(h) * Np + t0) * D + 8 * q.c;
 #pragma unroll
       for (int i = 0; i < kRows; ++i) {
         float x[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = kr[i][e] * sk;
-        *reinterpret_cast<uint2*>(K8 + (static_cast<int64_t>(h) * Np + t0 + i) * D + 8 * q.c) = fp8_pack8(x);
+        *reinterpret_cast<uint2*>(page + k8row + i * D) = fp8_pack8(x);
       }
       // Vt rows: 8 consecutive tokens of one value dim
+      const uint32_t v8row = (static_cast<uint32_t>(h) * D + 8 * q.c) * Np + t0;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int64_t off = (static_cast<int64_t>(h) * D + 8 * q.c + e) * Np + t0;
         if (kBf16V) {
-          *reinterpret_cast<bf16x8*>(reinterpret_cast<__bf16*>(V8) + off) = vt[e];
+          st16(page, v8_part + (v8row + e * Np) * 2u, vt[e]);
         } else {
           float x[8];
 #pragma unroll
           for (int i = 0; i < kRows; ++i) x[i] = static_cast<float>(vt[e][i]) * sv;
-          *reinterpret_cast<uint2*>(V8 + off) = fp8_pack8(x);
+          *reinterpret_cast<uint2*>(page + v8_part + v8row + e * Np) = fp8_pack8(x);
         }
-        if (capture && t0 < N) *reinterpret_cast<bf16x8*>(ancVt + vrow + int64_t(e) * N) = vt[e];
+        if (capture && valid) st16(a.anchor_raw, vrow + e * N * 2u, vt[e]);
       }
       if (q.g == 0 && q.c == 0) {
         const uint16_t code = static_cast<uint16_t>((ek + 127) | ((ev + 127) << 8));
-        *reinterpret_cast<uint16_t*>(codes + (static_cast<int64_t>(h) * a.T + tile) * 2) = code;
+        *reinterpret_cast<uint16_t*>(page + code_part + (static_cast<uint32_t>(h) * a.T + tile) * 2u) = code;
       }
     }
     __syncthreads();                            // red is rewritten by the next pass
   }
 }
 
-// Heads per work-group: a multiple of the heads one pass covers, few enough
-// groups that each work-group reuses its angles over several heads, enough
-// that the grid holds about four work-groups per compute unit.
-int heads_per_group(int H, int hpp, int blocks) {
-  const int want_groups = (1024 + blocks - 1) / blocks;
-  const int max_groups = (H + hpp - 1) / hpp;
-  const int groups = want_groups < 1 ? 1 : (want_groups > max_groups ? max_groups : want_groups);
-  int hpg = (H + groups - 1) / groups;
-  hpg = (hpg + hpp - 1) / hpp * hpp;
-  return hpg;
-}
+// Heads per work-group: the heads one pass covers (two at D = 128).  Walking
+// more heads per work-group reuses the block's angle table longer but leaves
+// fewer work-groups to hide memory latency: on the 1.3B round one pass per
+// work-group (2664 work-groups) measured 0.103 ms per launch against 0.109 ms
+// with two or four passes.
+int heads_per_group(int hpp) { return hpp; }
 
 }  // namespace
 
+size_t publish_lds_bytes(int F, int Hh, int Ww, int D, int nt) {
+  const int hw = Hh * Ww;
+  const int frames = (kTokens - 1) / hw + 2 < F ? (kTokens - 1) / hw + 2 : F;
+  return (size_t(kTokens) * (D / 2) + size_t(frames) * nt) * sizeof(float2);
+}
+
 hipError_t launch_publish(const PublishArgs& args, int dtype, hipStream_t stream) {
   if (args.n_tasks <= 0) return hipSuccess;
-  if (args.nt > kMaxFramePairs) return hipErrorInvalidValue;
   PublishArgs a = args;
+  const size_t lds = publish_lds_bytes(a.F, a.Hh, a.Ww, a.D, a.nt);
+  if (lds > kPublishMaxLds) return hipErrorInvalidValue;
   const int vec = dtype == WF_F32 ? 4 : 8;
   const int hpp = kThreads / (kRows * (a.D / vec));
   if (hpp < 1 || a.D % vec != 0) return hipErrorInvalidValue;
   if (dtype == WF_FP8 || dtype == WF_FP8K) {
     if (a.D != kFp8D) return hipErrorInvalidValue;
-    a.heads_per_group = heads_per_group(a.H, hpp, a.T * a.n_tasks);
+    a.heads_per_group = heads_per_group(hpp);
     const dim3 grid(a.T, (a.H + a.heads_per_group - 1) / a.heads_per_group, a.n_tasks);
-    if (dtype == WF_FP8) hipLaunchKernelGGL(wf_publish_fp8_kernel<false>, grid, dim3(kThreads), 0, stream, a);
-    else hipLaunchKernelGGL(wf_publish_fp8_kernel<true>, grid, dim3(kThreads), 0, stream, a);
+    if (dtype == WF_FP8) hipLaunchKernelGGL(wf_publish_fp8_kernel<false>, grid, dim3(kThreads), lds, stream, a);
+    else hipLaunchKernelGGL(wf_publish_fp8_kernel<true>, grid, dim3(kThreads), lds, stream, a);
     return hipGetLastError();
   }
   const int blocks = (a.N + kTokens - 1) / kTokens;
-  a.heads_per_group = heads_per_group(a.H, hpp, blocks * a.n_tasks);
+  a.heads_per_group = heads_per_group(hpp);
   const dim3 grid(blocks, (a.H + a.heads_per_group - 1) / a.heads_per_group, a.n_tasks);
   if (dtype == WF_BF16) {
-    hipLaunchKernelGGL(wf_publish_kernel<__bf16>, grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(wf_publish_kernel<__bf16>, grid, dim3(kThreads), lds, stream, a);
   } else {
-    hipLaunchKernelGGL(wf_publish_kernel<float>, grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(wf_publish_kernel<float>, grid, dim3(kThreads), lds, stream, a);
   }
   return hipGetLastError();
 }

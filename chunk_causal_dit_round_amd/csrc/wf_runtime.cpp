@@ -40,6 +40,12 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Kernel support for a valid config (checked at bind time so that plans of
 // any valid config can be built without a device).
 wf_status check_supported(const wf::Shape& sh) {
+  if (wf::publish_lds_bytes(sh.F, sh.Hh, sh.Ww, sh.D, sh.nt) > wf::kPublishMaxLds)
+    return fail(WF_EUNSUPPORTED, "publish: the angle tables of a 64-token block exceed its LDS");
+  // The publish kernels address one layer's slots, inputs and anchor store
+  // with 32-bit byte offsets.
+  if (double(sh.n_slots) * double(sh.page_bytes) >= 4294967296.0)
+    return fail(WF_EUNSUPPORTED, "one layer's slot pool must stay below 4 GiB");
   if (sh.dtype == WF_BF16) {
     if (sh.D != 64 && sh.D != 128)
       return fail(WF_EUNSUPPORTED, "bf16 kernels need head_dim 64 or 128");

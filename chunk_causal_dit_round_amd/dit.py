@@ -32,6 +32,11 @@ class DitSession:
         self.work_bytes = wf.wf_dit_workspace_bytes(s.h, self.dc)
         self.work = torch.empty(self.work_bytes, dtype=torch.uint8, device=dev)
 
+    def tune(self, stream=None) -> None:
+        """Pick the fastest hipBLASLt algorithm of each full-width product
+        (blocking; overwrites the work buffer)."""
+        wf.wf_dit_tune(self.s.h, self.dc, self.weights, self.work, self.work_bytes, stream)
+
     def load_x0(self, rnd: int, stages=None) -> None:
         """x of every (or the given) stage <- the round's seeded layer-0 input."""
         for st in (range(self.s.S + 1) if stages is None else stages):

@@ -108,6 +108,8 @@ def _load():
         "wf_dit_workspace_bytes": (i32, [H, ctypes.POINTER(wf_dit_config), ctypes.POINTER(sz)]),
         "wf_dit_layer": (i32, [H, ctypes.POINTER(wf_plan), i32, ctypes.POINTER(wf_dit_config),
                                ctypes.POINTER(wf_dit_weights), cvp, vp, vp, sz, vp]),
+        "wf_dit_tune": (i32, [H, ctypes.POINTER(wf_dit_config), ctypes.POINTER(wf_dit_weights), vp, sz,
+                              vp]),
         "wf_dit_round": (i32, [H, ctypes.POINTER(wf_plan), ctypes.POINTER(wf_dit_config),
                                ctypes.POINTER(wf_dit_weights), cvp, vp, vp, sz, vp]),
     }
@@ -268,6 +270,11 @@ def wf_dit_layer(h, plan, layer, dc, weights, mod, x, work, work_bytes, stream=N
     w = weights[layer] if isinstance(weights, ctypes.Array) else weights
     _check(_lib.wf_dit_layer(h, ctypes.byref(plan), layer, ctypes.byref(dc), ctypes.byref(w),
                              _ptr(mod), _ptr(x), _ptr(work), work_bytes, _stream(stream)))
+
+
+def wf_dit_tune(h, dc, weights, work, work_bytes, stream=None):
+    """``weights``: an array of wf_dit_weights (element 0 is used)."""
+    _check(_lib.wf_dit_tune(h, ctypes.byref(dc), weights, _ptr(work), work_bytes, _stream(stream)))
 
 
 def wf_dit_round(h, plan, dc, weights, mod, x, work, work_bytes, stream=None):

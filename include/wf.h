@@ -310,6 +310,12 @@ wf_status wf_kv_publish(wf_handle* h, const wf_plan* plan, int32_t layer,
  * wf_set_attention_split).  d_q_rot: [S+1][N][H][D] from wf_kv_publish;
  * d_out: [S+1][N][H][D].
  * WF_EORDER if this layer was not published in this round.
+ * Numerics (bf16): the kernel multiplies each bf16 q_rot row by
+ * scale * log2(e) and rounds the product to bf16 again (the scores then come
+ * out in base-2 units), so every score carries two bf16 roundings of q and
+ * one of K: its error grows with the score's magnitude (about 2^-8 of it per
+ * rounding), not only with the output's.  fp32 accumulation; the softmax
+ * weights are rounded to bf16 for the P V product and the row sum alike.
  * Stream order: every attention call of a handle (of any layer and round,
  * and wf_dit_layer's, which calls this) uses the one split scratch of the
  * handle's table buffer unless the handle's split mode is WF_SPLIT_OFF or

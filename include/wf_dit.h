@@ -100,6 +100,20 @@ wf_status wf_dit_round(wf_handle* h, const wf_plan* plan, const wf_dit_config* d
                        const wf_dit_weights* w, const void* d_mod, void* d_x,
                        void* d_work, size_t work_bytes, void* stream);
 
+/* For callers that time the block or run it for long (benchmarks, serving
+ * warm-up): times the hipBLASLt heuristic's first WF_DIT_TUNE_CANDIDATES
+ * algorithms for each of the block's four products (QKV, output, FFN1,
+ * FFN2) at the full-width shape, (S + 1) N rows, on the caller's buffers
+ * (layer 0's weights w[0]; the work buffer's contents are overwritten), and
+ * keeps the fastest for later products of that shape on this handle; other
+ * shapes (fill and drain rounds) keep the heuristic's first choice.  Unlike
+ * every other call it synchronises `stream` (it reads HIP events).  Outputs
+ * then differ from the untuned block only by the products' rounding order.
+ * Errors as wf_dit_layer; WF_EDEVICE if a product or an event fails. */
+#define WF_DIT_TUNE_CANDIDATES 8
+wf_status wf_dit_tune(wf_handle* h, const wf_dit_config* dc, const wf_dit_weights* w,
+                      void* d_work, size_t work_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

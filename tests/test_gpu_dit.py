@@ -111,10 +111,16 @@ SMALL = [
 ]
 
 
+@pytest.mark.parametrize("tune", [False, True], ids=["heuristic", "tuned"])
 @pytest.mark.parametrize("w,ffn", SMALL, ids=[w.name for w, _ in SMALL])
-def test_small_dit_every_round(w, ffn):
+def test_small_dit_every_round(w, ffn, tune):
+    """Every round against the oracle; with ``tuned`` the products run the
+    algorithms wf_dit_tune timed fastest (the same bar: only the rounding
+    order of the products changes)."""
     s = Session(w.config(), io=False)
     ds = DitSession(s, ffn, tag=w.name)
+    if tune:
+        ds.tune()
     orc = _oracle_rounds(ds, w)
     worst = 0.0
     try:
