@@ -78,7 +78,7 @@ PAGE_KINDS = {
 # traffic comes from: FETCH_SIZE + WRITE_SIZE per launch, scaled by a device
 # copy of known size.
 TRAFFIC_FILES = {
-    "wan1.3b_4step": "attention_bf16_wan1.3b_4step_hbm_traffic.txt",
+    "wan1.3b_4step": "attention_bf16_wan1.3b_4step_kernel_trace_and_traffic.txt",
     "wan1.3b_4step_fp8": "attention_fp8_wan1.3b_4step_kernel_trace_and_traffic.txt",
     "wan1.3b_4step_fp8k": "attention_fp8k_wan1.3b_4step_kernel_trace_and_traffic.txt",
     "wan1.3b_5step": "attention_bf16_wan1.3b_5step_kernel_trace_and_traffic.txt",
