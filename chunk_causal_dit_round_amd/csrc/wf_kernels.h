@@ -40,6 +40,8 @@ struct PublishArgs {
   int32_t N, H, D, F, Hh, Ww;
   int32_t nt, nh, nw;
   int32_t heads_per_group;  // set by the launcher
+  int32_t frames_max;       // set by the launcher: frames a 64-token block can span
+  int32_t pad0_;
   int32_t Npad, T;        // FP8 pages: tokens padded to 64 T, T tiles
   int32_t n_tasks;
   int32_t pad_;
@@ -95,9 +97,9 @@ constexpr int kAttnBM_f32 = 64;
 constexpr int kFp8MaxCtxTiles = 4096;
 
 // The publish kernels stage a 64-token block's rotation angles in LDS: the
-// cos/sin of every (token, pair) of the block, and the frame axis's at the
-// frames the block spans.  Bytes of those tables, and the most allowed.
-size_t publish_lds_bytes(int F, int Hh, int Ww, int D, int nt);
+// frame axis's cos/sin at the frames the block spans, then the row and
+// column tables.  Bytes of that table, and the most allowed.
+size_t publish_lds_bytes(int F, int Hh, int Ww, int nt, int nh, int nw);
 constexpr size_t kPublishMaxLds = 60 * 1024;
 
 hipError_t launch_publish(const PublishArgs& a, int dtype, hipStream_t stream);

@@ -12,10 +12,10 @@
 // at D = 128).  A thread owns 8 consecutive tokens x one 16-byte chunk of a
 // head row (8 bf16 / 4 fp32 elements):
 //   * the rotation angles depend on the token and the pair, not on the head:
-//     the work-group stages the cos/sin of every (token, pair) of its block
-//     in LDS once, for all its heads; the frame axis's come from the absolute
-//     frame position, computed in fp64 (so positions are not bounded by the
-//     length of a table), the row and column axes' from fixed tables;
+//     the work-group stages its block's angle table in LDS once, for all its
+//     heads: the frame axis's cos/sin computed in fp64 from the absolute frame
+//     position (so positions are not bounded by the length of a table), the
+//     row and column axes' copied from fixed tables;
 //   * a thread issues all 24 row loads of a head (q, k, v) before it uses
 //     any, with no branch between them (the rows of a token group are valid
 //     together: N % 8 == 0 for bf16, FP8 and FP8K; fp32 clamps its rows);
@@ -71,15 +71,16 @@ __device__ inline Geom geom(int D, int vec) {
   return q;
 }
 
-// Angle tables of the work-group in LDS (float2 cos/sin):
-//   ctab [64][P]    every (token of the block, pair): the thread reads its
-//                   token's VEC / 2 consecutive pairs with immediate offsets
-//   ftab [frames_max][nt] the frame axis at the frames the block spans,
-//                   computed in fp64 from the absolute frame position (so
-//                   positions are not bounded by a table's length)
-// The row and column axes come from the fixed rope_hw tables.
-__device__ inline void stage_angles(const PublishArgs& a, int frame0, int tok0, float2* ctab,
-                                    float2* ftab) {
+// Angle table of the work-group in LDS (float2 cos/sin):
+//   [0, frames_max nt)            the frame axis at the frames the block
+//                                 spans, computed in fp64 from the absolute
+//                                 frame position (positions are not bounded
+//                                 by a table's length)
+//   [rows0, rows0 + Hh nh)        the row axis        } copied from the fixed
+//   [cols0, cols0 + Ww nw)        the column axis     } rope_hw tables
+// The copy issues eight independent loads per thread before it stores any.
+// Returns f_lo, the first frame (within the chunk) the block spans.
+__device__ inline int stage_angles(const PublishArgs& a, int frame0, int tok0, float2* tab) {
   const int hw = a.Hh * a.Ww;
   const int last = min(tok0 + kTokens, a.N) - 1;
   const int f_lo = tok0 / hw;
@@ -89,38 +90,73 @@ __device__ inline void stage_angles(const PublishArgs& a, int frame0, int tok0, 
     const double ang = static_cast<double>(static_cast<int64_t>(frame0) + f_lo + f) * a.omega_t[m];
     double s, c;
     sincos(ang, &s, &c);
-    ftab[i] = make_float2(static_cast<float>(c), static_cast<float>(s));
+    tab[i] = make_float2(static_cast<float>(c), static_cast<float>(s));
+  }
+  constexpr int kBatch = 8;
+  const int n_hw = a.Hh * a.nh + a.Ww * a.nw;
+  float2* dst = tab + a.frames_max * a.nt;
+  for (int i0 = threadIdx.x; i0 < n_hw; i0 += kBatch * kThreads) {
+    float2 v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) v[u] = a.rope_hw[min(i0 + u * kThreads, n_hw - 1)];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (i0 + u * kThreads < n_hw) dst[i0 + u * kThreads] = v[u];
   }
   __syncthreads();
-  // Four threads per token: one token's position is decoded once, then each
-  // thread fills every fourth pair of the token's row.
-  const int P = a.D / 2;
-  static_assert(kThreads == 4 * kTokens, "four threads per token");
-  {
-    const int r = threadIdx.x >> 2, p0 = threadIdx.x & 3;
-    const int tok = min(tok0 + r, a.N - 1);                    // rows past N are never stored
-    const int f = tok / hw - f_lo, y = (tok / a.Ww) % a.Hh, x = tok % a.Ww;
-    const float2* fr = ftab + f * a.nt;                        // LDS
-    const float2* yr = a.rope_hw + y * a.nh - a.nt;            // row table [Hh][nh]
-    const float2* xr = a.rope_hw + a.Hh * a.nh + x * a.nw - (a.nt + a.nh);   // column table
-    float2* out = ctab + r * P;
-    for (int p = p0; p < P; p += 4) {
-      if (p < a.nt) {
-        out[p] = fr[p];
-      } else if (p < a.nt + a.nh) {
-        out[p] = yr[p];
-      } else {
-        out[p] = xr[p];
+  return f_lo;
+}
+
+// A thread's view of the angle table.  Its tokens are walked in order (the
+// column steps, wrapping into the next row and frame), and the table index
+// of pair p of the current token is base + p, the base chosen by p's axis.
+struct Pos {
+  int f, y, x;
+};
+
+template <int VEC>
+struct Angles {
+  int f_lo, f_last, p0, rows0, cols0;
+  Pos first;
+
+  __device__ Angles(const PublishArgs& a, int f_lo_, int t0, int c) {
+    const int hw = a.Hh * a.Ww;
+    f_lo = f_lo_;
+    f_last = (min(t0 + kRows, a.N) - 1) / hw;      // the last frame staged for this thread
+    p0 = c * VEC / 2;
+    rows0 = a.frames_max * a.nt;
+    cols0 = rows0 + a.Hh * a.nh;
+    const int rem = t0 - (t0 / hw) * hw;
+    first = Pos{t0 / hw, rem / a.Ww, rem - (rem / a.Ww) * a.Ww};
+  }
+
+  __device__ static void next(const PublishArgs& a, Pos& q) {
+    if (++q.x == a.Ww) {
+      q.x = 0;
+      if (++q.y == a.Hh) {
+        q.y = 0;
+        ++q.f;
       }
     }
   }
-  __syncthreads();
-}
+
+  // cos/sin of the thread's pairs at position q
+  __device__ void get(const PublishArgs& a, const float2* tab, const Pos& q, float2 (&cs)[VEC / 2]) const {
+    const int bf = (min(q.f, f_last) - f_lo) * a.nt;
+    const int by = rows0 + q.y * a.nh - a.nt;
+    const int bx = cols0 + q.x * a.nw - (a.nt + a.nh);
+#pragma unroll
+    for (int e = 0; e < VEC / 2; ++e) {
+      const int p = p0 + e;
+      cs[e] = tab[(p < a.nt ? bf : (p < a.nt + a.nh ? by : bx)) + p];
+    }
+  }
+};
 
 // Rotated pairs (x_2e, x_2e+1) -> (x0 cos - x1 sin, x0 sin + x1 cos), fp32;
-// cs = the row's VEC / 2 consecutive (cos, sin) pairs.
+// cs = the row's VEC / 2 (cos, sin) pairs.
 template <int VEC, typename R>
-__device__ inline void rotate_f32(const R& x, const float2* cs, float (&out)[VEC]) {
+__device__ inline void rotate_f32(const R& x, const float2 (&cs)[VEC / 2], float (&out)[VEC]) {
 #pragma unroll
   for (int e = 0; e < VEC / 2; ++e) {
     const float2 w = cs[e];
@@ -131,7 +167,8 @@ __device__ inline void rotate_f32(const R& x, const float2* cs, float (&out)[VEC
 }
 
 template <typename T>
-__device__ inline typename Vec<T>::raw rotate(const typename Vec<T>::raw& x, const float2* cs) {
+__device__ inline typename Vec<T>::raw rotate(const typename Vec<T>::raw& x,
+                                              const float2 (&cs)[Vec<T>::n / 2]) {
   constexpr int VEC = Vec<T>::n;
   float r[VEC];
   rotate_f32<VEC>(x, cs, r);
@@ -164,16 +201,15 @@ __global__ __launch_bounds__(kThreads) void wf_publish_kernel(const PublishArgs 
   const int tok0 = blockIdx.x * kTokens;
   const int hg0 = blockIdx.y * a.heads_per_group;
   const int hg1 = min(a.H, hg0 + a.heads_per_group);
-  const int N = a.N, H = a.H, D = a.D, P = D / 2;
-  float2* ctab = lds_tab;
-  stage_angles(a, task.frame0, tok0, ctab, lds_tab + kTokens * P);
+  const int N = a.N, H = a.H, D = a.D;
+  const int f_lo = stage_angles(a, task.frame0, tok0, lds_tab);
   const Geom q = geom(D, VEC);
   const int t0 = tok0 + kRows * q.g;
   // Rows of the group are valid together (bf16: N % 8 == 0) or, for fp32
   // (N % 4 == 0), the first four alone; loads clamp to row N - 1.
   if (q.slot >= q.hpp || t0 >= N) return;
   const bool full = t0 + kRows <= N;
-  const float2* cs0 = ctab + (kRows * q.g) * P + (VEC / 2) * q.c;   // row i: cs0 + i P
+  const Angles<VEC> ang(a, f_lo, t0, q.c);
   uint32_t row[kRows];
 #pragma unroll
   for (int i = 0; i < kRows; ++i) row[i] = static_cast<uint32_t>(min(i, N - 1 - t0));
@@ -198,9 +234,15 @@ __global__ __launch_bounds__(kThreads) void wf_publish_kernel(const PublishArgs 
 #pragma unroll
         for (int j = 0; j < kPieces; ++j)
           xv[e][j] = ld16<raw>(a.anchor_raw, vrow + e * vstep + (full ? VEC * j * E : 0u));
+      Pos pos = ang.first;
 #pragma unroll
-      for (int i = 0; i < kRows; ++i)
-        if (full || i < VEC) st16(slot, krow + i * kstep, rotate<T>(xk[i], cs0 + i * P));
+      for (int i = 0; i < kRows; ++i) {
+        if (!full && i >= VEC) break;
+        float2 cs[VEC / 2];
+        ang.get(a, lds_tab, pos, cs);
+        st16(slot, krow + i * kstep, rotate<T>(xk[i], cs));
+        ang.next(a, pos);
+      }
 #pragma unroll
       for (int e = 0; e < VEC; ++e)
 #pragma unroll
@@ -216,12 +258,16 @@ __global__ __launch_bounds__(kThreads) void wf_publish_kernel(const PublishArgs 
       xk[i] = ld16<raw>(a.k, in0 + row[i] * in_step);
       xv[i] = ld16<raw>(a.v, in0 + row[i] * in_step);
     }
+    Pos pos = ang.first;
 #pragma unroll
     for (int i = 0; i < kRows; ++i) {
       if (!full && i >= VEC) break;             // fp32: the last four rows past N
-      st16(a.q_rot, in0 + i * in_step, rotate<T>(xq[i], cs0 + i * P));
-      st16(slot, krow + i * kstep, rotate<T>(xk[i], cs0 + i * P));
+      float2 cs[VEC / 2];
+      ang.get(a, lds_tab, pos, cs);
+      st16(a.q_rot, in0 + i * in_step, rotate<T>(xq[i], cs));
+      st16(slot, krow + i * kstep, rotate<T>(xk[i], cs));
       if (capture) st16(a.anchor_raw, krow + i * kstep, xk[i]);
+      ang.next(a, pos);
     }
     // Transposed write: element e of the chunk is value dim VEC c + e; its
     // 8 tokens go out as kPieces 16-byte pieces.
@@ -278,7 +324,7 @@ __device__ inline float wave_max(float v) {
 
 template <bool kBf16V>
 __global__ __launch_bounds__(kThreads) void wf_publish_fp8_kernel(const PublishArgs a) {
-  constexpr int D = kFp8D, P = kFp8D / 2;
+  constexpr int D = kFp8D;
   extern __shared__ float2 lds_tab[];
   __shared__ float red[kThreads / 64][2];
 
@@ -288,13 +334,12 @@ __global__ __launch_bounds__(kThreads) void wf_publish_fp8_kernel(const PublishA
   const int hg0 = blockIdx.y * a.heads_per_group;
   const int hg1 = min(a.H, hg0 + a.heads_per_group);
   const int N = a.N, H = a.H, Np = a.Npad;
-  float2* ctab = lds_tab;
-  stage_angles(a, task.frame0, tok0, ctab, lds_tab + kTokens * P);
+  const int f_lo = stage_angles(a, task.frame0, tok0, lds_tab);
   const Geom q = geom(D, 8);                    // two heads per pass, 2 waves each
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t0 = tok0 + kRows * q.g;
   const bool valid = t0 < N;                    // N % 8 == 0: all 8 rows or none
-  const float2* cs0 = ctab + (kRows * q.g) * P + 4 * q.c;
+  const Angles<8> ang(a, f_lo, valid ? t0 : N - kRows, q.c);
 
   char* page = static_cast<char*>(a.pool) + static_cast<int64_t>(task.slot) * a.page_bytes;
   const uint32_t v8_part = static_cast<uint32_t>(H) * Np * D;          // Vt after K8
@@ -323,8 +368,14 @@ __global__ __launch_bounds__(kThreads) void wf_publish_fp8_kernel(const PublishA
       for (int i = 0; i < kRows; ++i) xk[i] = ld16<bf16x8>(a.anchor_raw, krow + i * D * 2u);
 #pragma unroll
       for (int e = 0; e < 8; ++e) vt[e] = ld16<bf16x8>(a.anchor_raw, vrow + e * N * 2u);
+      Pos pos = ang.first;
 #pragma unroll
-      for (int i = 0; i < kRows; ++i) rotate_f32<8>(xk[i], cs0 + i * P, kr[i]);
+      for (int i = 0; i < kRows; ++i) {
+        float2 cs[4];
+        ang.get(a, lds_tab, pos, cs);
+        rotate_f32<8>(xk[i], cs, kr[i]);
+        ang.next(a, pos);
+      }
     } else if (act && valid) {
       const uint32_t in0 = (((static_cast<uint32_t>(task.stage) * N + t0) * H + h) * D + 8 * q.c) * 2u;
       bf16x8 xq[kRows], xk[kRows], xv[kRows];
@@ -334,10 +385,14 @@ __global__ __launch_bounds__(kThreads) void wf_publish_fp8_kernel(const PublishA
         xk[i] = ld16<bf16x8>(a.k, in0 + i * in_step);
         xv[i] = ld16<bf16x8>(a.v, in0 + i * in_step);
       }
+      Pos pos = ang.first;
 #pragma unroll
       for (int i = 0; i < kRows; ++i) {
-        st16(a.q_rot, in0 + i * in_step, rotate<__bf16>(xq[i], cs0 + i * P));
-        rotate_f32<8>(xk[i], cs0 + i * P, kr[i]);
+        float2 cs[4];
+        ang.get(a, lds_tab, pos, cs);
+        ang.next(a, pos);
+        st16(a.q_rot, in0 + i * in_step, rotate<__bf16>(xq[i], cs));
+        rotate_f32<8>(xk[i], cs, kr[i]);
         if (capture) st16(a.anchor_raw, krow + i * D * 2u, xk[i]);
       }
 #pragma unroll
@@ -408,16 +463,20 @@ int heads_per_group(int hpp) { return hpp; }
 
 }  // namespace
 
-size_t publish_lds_bytes(int F, int Hh, int Ww, int D, int nt) {
-  const int hw = Hh * Ww;
-  const int frames = (kTokens - 1) / hw + 2 < F ? (kTokens - 1) / hw + 2 : F;
-  return (size_t(kTokens) * (D / 2) + size_t(frames) * nt) * sizeof(float2);
+int publish_frames_max(int F, int Hh, int Ww) {
+  const int spans = (kTokens - 1) / (Hh * Ww) + 2;   // frames 64 consecutive tokens can touch
+  return spans < F ? spans : F;
+}
+
+size_t publish_lds_bytes(int F, int Hh, int Ww, int nt, int nh, int nw) {
+  return (size_t(publish_frames_max(F, Hh, Ww)) * nt + size_t(Hh) * nh + size_t(Ww) * nw) * sizeof(float2);
 }
 
 hipError_t launch_publish(const PublishArgs& args, int dtype, hipStream_t stream) {
   if (args.n_tasks <= 0) return hipSuccess;
   PublishArgs a = args;
-  const size_t lds = publish_lds_bytes(a.F, a.Hh, a.Ww, a.D, a.nt);
+  a.frames_max = publish_frames_max(a.F, a.Hh, a.Ww);
+  const size_t lds = publish_lds_bytes(a.F, a.Hh, a.Ww, a.nt, a.nh, a.nw);
   if (lds > kPublishMaxLds) return hipErrorInvalidValue;
   const int vec = dtype == WF_F32 ? 4 : 8;
   const int hpp = kThreads / (kRows * (a.D / vec));

@@ -40,8 +40,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Kernel support for a valid config (checked at bind time so that plans of
 // any valid config can be built without a device).
 wf_status check_supported(const wf::Shape& sh) {
-  if (wf::publish_lds_bytes(sh.F, sh.Hh, sh.Ww, sh.D, sh.nt) > wf::kPublishMaxLds)
-    return fail(WF_EUNSUPPORTED, "publish: the angle tables of a 64-token block exceed its LDS");
+  if (wf::publish_lds_bytes(sh.F, sh.Hh, sh.Ww, sh.nt, sh.nh, sh.nw) > wf::kPublishMaxLds)
+    return fail(WF_EUNSUPPORTED, "publish: the RoPE tables of a 64-token block (frames, rows, columns) exceed its LDS");
   // The publish kernels address one layer's slots, inputs and anchor store
   // with 32-bit byte offsets.
   if (double(sh.n_slots) * double(sh.page_bytes) >= 4294967296.0)
