@@ -235,10 +235,14 @@ def test_small_dit_over_fp8_pages_every_round(w, ffn, rel_tol):
         s.close()
 
 
-def test_full_size_wan13b_one_layer_fp8k_sampled():
-    """1.3B shape, one layer, over 8-bit-key pages: rounds 0..S+1, 48
-    sampled rows per active cell of the last round against the oracle."""
-    w = WAN13B_4STEP.with_(name="dit_wan1.3b_l1_fp8k", n_layers=1, dtype=wf.WF_FP8K)
+@pytest.mark.parametrize("dtype,rel_tol", [(wf.WF_FP8K, REL_TOL_FP8K), (wf.WF_FP8, REL_TOL_FP8)],
+                         ids=["fp8k", "fp8"])
+def test_full_size_wan13b_one_layer_8bit_pages_sampled(dtype, rel_tol):
+    """1.3B shape, one layer, over 8-bit-key pages (FP8K) and 8-bit K/V
+    pages (FP8): rounds 0..S+1, 48 sampled rows per active cell of the last
+    round against the oracle."""
+    tag = "fp8k" if dtype == wf.WF_FP8K else "fp8"
+    w = WAN13B_4STEP.with_(name=f"dit_wan1.3b_l1_{tag}", n_layers=1, dtype=dtype)
     s = Session(w.config(), io=False)
     ds = DitSession(s, 8960, tag=w.name)
     orc = _oracle_rounds(ds, w)
@@ -257,7 +261,7 @@ def test_full_size_wan13b_one_layer_fp8k_sampled():
             rows[-1] = w.n_tokens - 1
             want = orc.layer_output(last, 0, st, rows=rows)
             x_in = orc.x_in(last, 0, st)[rows]
-            worst = max(worst, _compare(got[st][rows], want, x_in, f"stage {st}", REL_TOL_FP8K))
+            worst = max(worst, _compare(got[st][rows], want, x_in, f"stage {st}", rel_tol))
         _log(f"{w.name}: worst err/bound {worst:.3f}")
     finally:
         s.close()
