@@ -22,12 +22,13 @@
 //     the B operand bytes of the PV product (P^T, k = key), no lane exchange;
 //   * O^T = Vt P^T, A = Vt rows (value dims), keys contiguous.
 // Schedule: the 8 waves (32 query rows each) run in lockstep, one
-// work-group barrier per 64-key tile: an MFMA cluster (PV of tile t-1, row
-// sums, QK of tile t; 9 FP8 MFMAs) then the softmax of tile t and the
-// staging of tile t+2.  With the MFMA cluster this short, letting the two
-// waves of a SIMD drift between clusters measured as fast as the bf16
-// instance's ping-pong between wave groups, with one barrier per tile
-// instead of two.  K and Vt tiles live in a
+// work-group barrier per 64-key tile.  The QK product runs one tile ahead
+// of the softmax: in step t a wave stages tile t+2, issues PV of tile t-1
+// and the row sums (5 FP8 MFMAs) among the row max of S(t), and issues QK of
+// tile t+1 (4 MFMAs) among the exponentials of tile t, so the matrix core
+// works while the wave's VALU runs the softmax, and the softmax never waits
+// for the scores it uses.  The scores of two consecutive tiles live in two
+// register sets that swap roles every step.  K and Vt tiles live in a
 // 4-stage LDS ring with 16-byte chunks XOR-swizzled per row (conflict-free
 // operand reads and stores).  Softmax in base 2 with lazy rescale; the QK
 // accumulators start from 2^7 divided by the running max (in exponent
@@ -217,7 +218,7 @@ __global__ __launch_bounds__(kNT, 1) void wf_attention_fp8_kernel(const AttnArgs
   f32x16 oacc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) oacc[i] = f32x16{};
-  f32x16 sacc[2];
+  f32x16 sA[2], sB[2];                            // S^T of two consecutive tiles
   f32x16 lacc = f32x16{};                         // row sums: ones x P^T
   i32x8 pf = {};
   i32x8 ones;
@@ -229,85 +230,84 @@ __global__ __launch_bounds__(kNT, 1) void wf_attention_fp8_kernel(const AttnArgs
   bool first_tile = true;
   int kcode = kE8M0One, vcode = kE8M0One;         // scales of the tiles in use
 
-  // ---- MFMA cluster: O^T += Vt(t-1) P(t-1)^T, then S^T(t) = K(t) Q^T ----
-  constexpr int kAhead = 2;
-  auto mfma_cluster = [&](int pv_stage, int qk_stage) {
-    const uint8_t* vb = lds + pv_stage * kStage;
-    const uint8_t* kb = lds + qk_stage * kStage;
-    auto frag = [&](int i) -> i32x8 {
-      const uint8_t* p0;
-      const uint8_t* p1;
-      if (i < 4) {
-        p0 = vb + va[i][0];
-        p1 = vb + va[i][1];
-      } else {
-        const int j = i - 4, s = j >> 1, t2 = j & 1;
-        p0 = kb + ka[t2][s][0];
-        p1 = kb + ka[t2][s][1];
-      }
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(p0);
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(p1);
-      i32x8 r;
+  // one 32-byte operand fragment from two 16-byte LDS chunks
+  auto frag = [&](const uint8_t* p0, const uint8_t* p1) -> i32x8 {
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(p0);
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(p1);
+    i32x8 r;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        r[e] = static_cast<int>(lo[e]);
-        r[4 + e] = static_cast<int>(hi[e]);
-      }
-      return r;
-    };
-    constexpr int NI = 8;
-    i32x8 fr[kAhead + 1];
-#pragma unroll
-    for (int i = 0; i < kAhead; ++i) fr[i] = frag(i);
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      if (i + kAhead < NI) fr[(i + kAhead) % (kAhead + 1)] = frag(i + kAhead);
-      const i32x8 f = fr[i % (kAhead + 1)];
-      if (i < 4) {
-        oacc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f, pf, oacc[i], 0, 0, 0, vcode, 0,
-                                                                  kE8M0One);
-        if (i == 3)
-          lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pf, lacc, 0, 0, 0, kE8M0One, 0,
-                                                                 kE8M0One);
-      } else {
-        const int j = i - 4, s = j >> 1, t2 = j & 1;
-        sacc[t2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f, qf[s], s == 0 ? moff : sacc[t2],
-                                                                   0, 0, 0, kcode, 0, qscale);
-      }
+    for (int e = 0; e < 4; ++e) {
+      r[e] = static_cast<int>(lo[e]);
+      r[4 + e] = static_cast<int>(hi[e]);
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);
+    return r;
+  };
+  // ---- O^T += Vt(t-1) P(t-1)^T and the row sums (ones x P^T) ----
+  auto pv_cluster = [&](int pv_stage) {
+    const uint8_t* vb = lds + pv_stage * kStage;
+    i32x8 fr[4];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i == 3) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i + kAhead < NI) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    for (int i = 0; i < 4; ++i) fr[i] = frag(vb + va[i][0], vb + va[i][1]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      oacc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fr[i], pf, oacc[i], 0, 0, 0, vcode, 0, kE8M0One);
+    lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pf, lacc, 0, 0, 0, kE8M0One, 0, kE8M0One);
+  };
+  // ---- S^T = K Q^T of one tile into sn, from the current moff ----
+  auto qk_issue = [&](int qk_stage, f32x16 (&sn)[2]) {
+    const uint8_t* kb = lds + qk_stage * kStage;
+    i32x8 fr[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int s2 = j >> 1, t2 = j & 1;
+      fr[j] = frag(kb + ka[t2][s2][0], kb + ka[t2][s2][1]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int s2 = j >> 1, t2 = j & 1;
+      sn[t2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fr[j], qf[s2], s2 == 0 ? moff : sn[t2], 0, 0, 0,
+                                                              kcode, 0, qscale);
     }
   };
-
-  // ---- VALU cluster: online softmax of S(t) (base 2, lazy rescale) ----
-  // Value v of sacc[t2] in lane (col, half) is key 32 half + 16 t2 + v.
-  auto softmax = [&](int valid) {
+  // ---- online softmax of sc = S(t) (base 2, lazy rescale), with PV of
+  // tile t-1 among its row max and QK of tile t+1 into sn among its
+  // exponentials.  QK is issued after the rescale decision, so it starts
+  // from the moved m.  Value v of sc[t2] in lane (col, half) is key
+  // 32 half + 16 t2 + v. ----
+  auto softmax = [&](int valid, f32x16 (&sc)[2], f32x16 (&sn)[2], int qk_stage, int pv_stage) {
     if (valid < kBN) {
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
         for (int v = 0; v < 16; ++v)
-          if (32 * half + 16 * t2 + v >= valid) sacc[t2][v] = -__builtin_inff();
+          if (32 * half + 16 * t2 + v >= valid) sc[t2][v] = -__builtin_inff();
     }
+    pv_cluster(pv_stage);
     // max of the lane's 32 values (S - m + kBias) as a tree of 3-input maxima
     float r[11];
 #pragma unroll
     for (int i = 0; i < 10; ++i) {
       const int a0 = 3 * i, a1 = 3 * i + 1, a2 = 3 * i + 2;
-      r[i] = fmaxf(fmaxf(sacc[a0 >> 4][a0 & 15], sacc[a1 >> 4][a1 & 15]), sacc[a2 >> 4][a2 & 15]);
+      r[i] = fmaxf(fmaxf(sc[a0 >> 4][a0 & 15], sc[a1 >> 4][a1 & 15]), sc[a2 >> 4][a2 & 15]);
     }
-    r[10] = fmaxf(sacc[1][14], sacc[1][15]);
+    r[10] = fmaxf(sc[1][14], sc[1][15]);
     const float r0 = fmaxf(fmaxf(r[0], r[1]), r[2]), r1 = fmaxf(fmaxf(r[3], r[4]), r[5]);
     const float r2 = fmaxf(fmaxf(r[6], r[7]), r[8]), r3 = fmaxf(r[9], r[10]);
     const float mx = pair_max32(fmaxf(fmaxf(r0, r1), fmaxf(r2, r3))) - kBias;   // max S - m
+    // order: the 8 Vt operand reads, then each PV MFMA with 3 VALU ops of
+    // the row max
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 1);
+    }
     // Lazy rescale: m moves only when some lane's max exceeds it by more
-    // than 2^kRescale (always on the first tile).
-    if (first_tile || __any(mx > kRescale)) {
+    // than 2^kRescale (always on the first tile).  (The vote and the flag
+    // are combined without a branch, which keeps the PV MFMAs in the row
+    // max's block.)
+    const bool grow = __any(mx > kRescale);
+    if (grow | first_tile) {
       const float up = first_tile ? mx : fmaxf(mx, 0.f);
       if (!first_tile) {
         const float alpha = __builtin_amdgcn_exp2f(-up);
@@ -319,26 +319,35 @@ __global__ __launch_bounds__(kNT, 1) void wf_attention_fp8_kernel(const AttnArgs
       first_tile = false;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        sacc[0][v] -= up;
-        sacc[1][v] -= up;
+        sc[0][v] -= up;
+        sc[1][v] -= up;
         moff[v] -= up;
       }
     }
+    qk_issue(qk_stage, sn);
     float p[2][16];
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) p[t2][v] = __builtin_amdgcn_exp2f(sacc[t2][v]);
+      for (int v = 0; v < 16; ++v) p[t2][v] = __builtin_amdgcn_exp2f(sc[t2][v]);
     // byte j = 16 t2 + v of the PV B operand
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
       const int t2 = w >> 2, v0 = 4 * (w & 3);
       pf[w] = static_cast<int>(pack4(p[t2][v0], p[t2][v0 + 1], p[t2][v0 + 2], p[t2][v0 + 3]));
     }
+    // order: the 8 K operand reads, then each QK MFMA with 10 VALU ops of
+    // the exponentials and the E4M3 packing
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
+    }
   };
 
   // ---- prologue: tiles 0..2 into stages 0..2; stage 3's Vt zeroed (the
-  // first cluster multiplies P = 0 with it) ----
+  // first step multiplies P = 0 with it); QK of tile 0 ----
   const int pre = n_tiles < kStages - 1 ? n_tiles : kStages - 1;
   for (int t = 0; t < pre; ++t) {
     load_next();
@@ -352,40 +361,55 @@ __global__ __launch_bounds__(kNT, 1) void wf_attention_fp8_kernel(const AttnArgs
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   kcode = tcode[0] & 0xff;
+  qk_issue(0, sA);
 
-  // One barrier per tile orders the LDS ring: a tile stored in the softmax
-  // phase of iteration t is first read two barriers later (cluster t+2), and
-  // the stage it overwrites was last read in cluster t-1, which every wave
-  // finished (LDS reads drained) before the barrier closing iteration t-1.
+  // One barrier per tile orders the LDS ring: step t stores tile t+2 into
+  // the stage that held tile t-2, whose last reader (PV in step t-1) every
+  // wave finished (LDS reads drained) before the barrier closing step t-1;
+  // tile t+1's K (read in step t) was stored in step t-1, and tile t-1's Vt
+  // (read in step t) in step t-3.  The QK of step n_tiles - 1 reads a stale
+  // stage; its scores are never used.
   bool staged = false;
   int ptp = 0;                                    // tile-in-page of the softmax's tile
-  for (int t = 0; t <= n_tiles; ++t) {
-    mfma_cluster((t - 1) & (kStages - 1), t & (kStages - 1));
-    if (t < n_tiles) {
-      if (staged) store_tile((t + 2) & (kStages - 1));
-      staged = false;
-      if (t + 3 < n_tiles) {
-        load_next();
-        staged = true;
-      }
-      softmax(ptp == T - 1 ? last_valid : kBN);
-      if (++ptp == T) ptp = 0;
-      // scales of the next cluster: QK of tile t+1, PV of tile t
-      const int nxt = t + 1 < n_tiles ? t + 1 : t;
-      kcode = tcode[nxt] & 0xff;
-      vcode = tcode[t] >> 8;
+  auto step = [&](int t, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+    if (staged) store_tile((t + 2) & (kStages - 1));
+    staged = false;
+    if (t + 3 < n_tiles) {
+      load_next();
+      staged = true;
     }
+    // scales: QK of tile t+1 now, PV of tile t in the next step
+    const int nxt = t + 1 < n_tiles ? t + 1 : t;
+    kcode = tcode[nxt] & 0xff;
+    softmax(ptp == T - 1 ? last_valid : kBN, sc, sn, (t + 1) & (kStages - 1), (t - 1) & (kStages - 1));
+    if (++ptp == T) ptp = 0;
+    vcode = tcode[t] >> 8;
+    // keep the QK MFMAs and the weights before the barrier (their results
+    // are used only after it; the compiler would sink them past it)
+    asm volatile("" : "+v"(sn[0]), "+v"(sn[1]), "+v"(pf));
     __builtin_amdgcn_sched_barrier(0); __syncthreads(); __builtin_amdgcn_sched_barrier(0);
+  };
+  for (int t = 0; t < n_tiles; t += 2) {         // the score sets swap roles every step
+    step(t, sA, sB);
+    if (t + 1 < n_tiles) step(t + 1, sB, sA);
   }
+  pv_cluster((n_tiles - 1) & (kStages - 1));      // PV of the last tile
 
   // ---- epilogue: O = (O^T)^T / l, or the half's partial result ----
+  // The lane's query row is derived again from the lane id (read by an asm
+  // statement the compiler cannot merge with the first read), so no
+  // register carries it through the tile loop.
+  uint32_t lane_e;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_e));
+  const int half_e = static_cast<int>(lane_e >> 5);
+  const int q_e = qt * BM + wave * 32 + static_cast<int>(lane_e & 31);
   if (G.part >= 0) {
-    if (q < N) store_partial(a, G.part, q, h, -moff[0], lacc[0], oacc, half);
+    if (q_e < N) store_partial(a, G.part, q_e, h, -moff[0], lacc[0], oacc, half_e);
     return;
   }
   const float inv = 1.f / lacc[0];
-  if (q < N) {
-    __bf16* orow = static_cast<__bf16*>(a.out) + ((static_cast<int64_t>(G.stage) * N + q) * H + h) * kD;
+  if (q_e < N) {
+    __bf16* orow = static_cast<__bf16*>(a.out) + ((static_cast<int64_t>(G.stage) * N + q_e) * H + h) * kD;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -393,7 +417,7 @@ __global__ __launch_bounds__(kNT, 1) void wf_attention_fp8_kernel(const AttnArgs
         bf16x4 o;
 #pragma unroll
         for (int j = 0; j < 4; ++j) o[j] = static_cast<__bf16>(oacc[dt][4 * i4 + j] * inv);
-        *reinterpret_cast<bf16x4*>(orow + 32 * dt + 8 * i4 + 4 * half) = o;
+        *reinterpret_cast<bf16x4*>(orow + 32 * dt + 8 * i4 + 4 * half_e) = o;
       }
   }
 }
