@@ -307,13 +307,13 @@ __global__ __launch_bounds__(kNT, 1) void wf_attention_fp8_kernel(const AttnArgs
     // are combined without a branch, which keeps the PV MFMAs in the row
     // max's block.)
     const bool grow = __any(mx > kRescale);
+    float alpha = 1.f;
+    bool rescale = false;                         // wave-uniform
     if (grow | first_tile) {
       const float up = first_tile ? mx : fmaxf(mx, 0.f);
       if (!first_tile) {
-        const float alpha = __builtin_amdgcn_exp2f(-up);
-        lacc *= alpha;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) oacc[i] *= alpha;
+        alpha = __builtin_amdgcn_exp2f(-up);
+        rescale = true;
       }
       // (before the first tile the accumulators start from 0, i.e. m = kBias)
       first_tile = false;
@@ -343,6 +343,13 @@ __global__ __launch_bounds__(kNT, 1) void wf_attention_fp8_kernel(const AttnArgs
     for (int j = 0; j < 4; ++j) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
+    }
+    // O and l take the new m at the end of the softmax: PV of tile t-1,
+    // issued among the row max, has finished by then
+    if (rescale) {
+      lacc *= alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) oacc[i] *= alpha;
     }
   };
 
