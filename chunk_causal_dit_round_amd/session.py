@@ -42,8 +42,11 @@ class Session:
                 for n in ("q", "k", "v", "q_rot", "out")}
 
     # ---- views of the slot pool (layouts documented in include/wf.h) ----
-    def _slot_bytes(self, layer: int, slot: int):
+    def slot_bytes(self, layer: int, slot: int):
+        """All bytes of one slot of one layer (uint8), whatever the page format."""
         return self.pool.view(self.L, self.n_slots, self.page_bytes)[layer, slot]
+
+    _slot_bytes = slot_bytes
 
     def page(self, layer: int, slot: int):
         """(K [H][N][D], Vt [H][D][N]) views of one slot of one layer."""

@@ -8,7 +8,7 @@
   calls of a handle run one after another (they share the handle's split
   scratch; include/wf.h states the rule).
 * Stale slots: slots a round neither reads nor writes may hold anything
-  (NaN here) without touching the outputs.
+  (NaN bytes here) without touching the outputs.
 * HIP graphs: a round's layers captured into a graph replay to the eager bits.
 """
 
@@ -41,8 +41,15 @@ def outputs(ro):
     return ro.sess.bufs["out"].clone()
 
 
-def test_causal_invariant_bit_identical():
-    w = W_INV
+DTYPES = [wf.WF_BF16, wf.WF_FP8, wf.WF_FP8K]
+DTYPE_IDS = ["bf16", "fp8", "fp8k"]
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=DTYPE_IDS)
+def test_causal_invariant_bit_identical(dtype):
+    """Over FP8 pages too: a chunk's page (and its per-tile scales) is its
+    own, so a noisier chunk's K/V cannot reach a cleaner stage."""
+    w = W_INV.with_(name=f"causal_{dtype}", dtype=dtype)
     k = 9  # full width, anchor present
     for j in range(w.S):
         pert = {(k, layer, j, n): 3.0 for layer in range(w.n_layers) for n in ("k", "v")}
@@ -90,8 +97,11 @@ def test_same_graph_any_issue_order_and_streams():
             ro.close()
 
 
-def test_stale_slots_do_not_matter():
-    w = W_INV
+@pytest.mark.parametrize("dtype", DTYPES, ids=DTYPE_IDS)
+def test_stale_slots_do_not_matter(dtype):
+    """Every byte of the slots a round does not use is 0xFF (NaN in bf16,
+    E4M3 and as an E8M0 scale code)."""
+    w = W_INV.with_(name=f"stale_{dtype}", dtype=dtype)
     oc = oracle_cfg(w)
     clean, poisoned = Rollout(w), Rollout(w)
     try:
@@ -102,9 +112,7 @@ def test_stale_slots_do_not_matter():
             for layer in range(w.n_layers):
                 for slot in range(oc.n_slots):
                     if slot not in live:
-                        K, Vt = poisoned.sess.page(layer, slot)
-                        K.fill_(float("nan"))
-                        Vt.fill_(float("nan"))
+                        poisoned.sess.slot_bytes(layer, slot).fill_(0xFF)
             clean.run(k)
             poisoned.run(k)
             a, b = outputs(clean), outputs(poisoned)
@@ -138,7 +146,7 @@ def test_order_errors_on_device():
         ro.close()
 
 
-@pytest.mark.parametrize("dtype", [wf.WF_BF16, wf.WF_FP8K], ids=["bf16", "fp8k"])
+@pytest.mark.parametrize("dtype", DTYPES, ids=DTYPE_IDS)
 def test_round_layers_replay_in_a_hip_graph(dtype):
     """The layers of a round (publish + attention per layer) captured into
     a HIP graph: every replay, with eager work and synchronisations between
