@@ -23,9 +23,9 @@
 //   * O^T = Vt P^T, A = Vt rows (value dims), keys contiguous.
 // Schedule: the 8 waves (32 query rows each) run in lockstep, one
 // work-group barrier per 64-key tile.  The QK product runs one tile ahead
-// of the softmax: in step t a wave stages tile t+2, issues PV of tile t-1
-// and the row sums (5 FP8 MFMAs) among the row max of S(t), and issues QK of
-// tile t+1 (4 MFMAs) among the exponentials of tile t, so the matrix core
+// of the softmax: in step t a wave issues PV of tile t-1 and the row sums
+// (5 FP8 MFMAs) among the row max of S(t), issues QK of tile t+1 (4 MFMAs)
+// among the exponentials of tile t, then stages tile t+2, so the matrix core
 // works while the wave's VALU runs the softmax, and the softmax never waits
 // for the scores it uses.  The scores of two consecutive tiles live in two
 // register sets that swap roles every step.  K and Vt tiles live in a
@@ -370,27 +370,31 @@ __global__ __launch_bounds__(kNT, 1) void wf_attention_fp8_kernel(const AttnArgs
   kcode = tcode[0] & 0xff;
   qk_issue(0, sA);
 
-  // One barrier per tile orders the LDS ring: step t stores tile t+2 into
-  // the stage that held tile t-2, whose last reader (PV in step t-1) every
-  // wave finished (LDS reads drained) before the barrier closing step t-1;
-  // tile t+1's K (read in step t) was stored in step t-1, and tile t-1's Vt
-  // (read in step t) in step t-3.  The QK of step n_tiles - 1 reads a stale
-  // stage; its scores are never used.
+  // One barrier per tile orders the LDS ring: at its end, step t stores
+  // tile t+2 (fetched at the end of step t-1, so its loads had a whole step
+  // to land) into the stage that held tile t-2, whose last reader (PV in
+  // step t-1) every wave finished (LDS reads drained) before the barrier
+  // closing step t-1; tile t+1's K (read in step t) was stored at the end
+  // of step t-1, and tile t-1's Vt (read in step t) at the end of step t-3.
+  // The QK of step n_tiles - 1 reads a stale stage; its scores are never
+  // used.
   bool staged = false;
   int ptp = 0;                                    // tile-in-page of the softmax's tile
   auto step = [&](int t, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
-    if (staged) store_tile((t + 2) & (kStages - 1));
-    staged = false;
-    if (t + 3 < n_tiles) {
-      load_next();
-      staged = true;
-    }
     // scales: QK of tile t+1 now, PV of tile t in the next step
     const int nxt = t + 1 < n_tiles ? t + 1 : t;
     kcode = tcode[nxt] & 0xff;
     softmax(ptp == T - 1 ? last_valid : kBN, sc, sn, (t + 1) & (kStages - 1), (t - 1) & (kStages - 1));
     if (++ptp == T) ptp = 0;
     vcode = tcode[t] >> 8;
+    // staging after the softmax: the LDS stores stay out of the operand
+    // reads' way, and a late load stalls the wave while its QK MFMAs run
+    if (staged) store_tile((t + 2) & (kStages - 1));
+    staged = false;
+    if (t + 3 < n_tiles) {
+      load_next();
+      staged = true;
+    }
     // keep the QK MFMAs and the weights before the barrier (their results
     // are used only after it; the compiler would sink them past it)
     asm volatile("" : "+v"(sn[0]), "+v"(sn[1]), "+v"(pf));
