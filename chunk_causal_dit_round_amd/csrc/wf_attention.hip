@@ -48,6 +48,7 @@
 #include <type_traits>
 
 #include "wf_kernels.h"
+#include "wf_items.h"
 #include "wf_partial.h"
 
 namespace wf {
@@ -110,8 +111,8 @@ __global__ __launch_bounds__(512, 1) void wf_attention_bf16_kernel(const AttnArg
 
   __shared__ __attribute__((aligned(16))) __bf16 lds[STAGES][KTILE + VTILE];
 
-  const int item = blockIdx.x;
-  if (item >= a.n_items) return;
+  if (static_cast<int>(blockIdx.x) >= a.n_items) return;
+  const int item = xcd_item(blockIdx.x, a.n_items, a.q_tiles);   // whole units per XCD
   const int g = find_group(a, item);
   const AttnGroup& G = a.grp[g];
   const int li = item - G.item0;

@@ -38,6 +38,7 @@
 #include <cstdint>
 
 #include "wf_kernels.h"
+#include "wf_items.h"
 #include "wf_partial.h"
 
 namespace wf {
@@ -109,8 +110,8 @@ __global__ __launch_bounds__(kNT, 1) void wf_attention_fp8k_kernel(const AttnArg
   __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * kStage];
   __shared__ uint8_t tcode[kFp8MaxCtxTiles];   // eK + 127 of every context tile
 
-  const int item = blockIdx.x;
-  if (item >= a.n_items) return;
+  if (static_cast<int>(blockIdx.x) >= a.n_items) return;
+  const int item = xcd_item(blockIdx.x, a.n_items, a.q_tiles);   // whole units per XCD
   const int g = find_group(a, item);
   const AttnGroup& G = a.grp[g];
   const int li = item - G.item0;
