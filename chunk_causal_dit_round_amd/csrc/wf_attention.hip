@@ -412,6 +412,26 @@ __global__ __launch_bounds__(512, 1) void wf_attention_bf16_kernel(const AttnArg
   __builtin_amdgcn_s_waitcnt(0);
   if (pgroup == 1) __syncthreads();
   bool staged = false;
+  // A wave whose 32 query rows all lie past N (the last query tile of a
+  // chunk) has no products to compute: it only stages its share of every
+  // tile and passes the same barriers, so its SIMD partner has the matrix
+  // core to itself.
+  if (__builtin_amdgcn_readfirstlane(qt * BM + wave * 32) >= N) {
+    for (int t = 0; t <= n_tiles; ++t) {
+      __syncthreads();
+      if (t < n_tiles) {
+        if (staged) store_tile((t + 2) & (STAGES - 1));
+        staged = false;
+        if (t + 3 < n_tiles) {
+          load_next();
+          staged = true;
+        }
+      }
+      __syncthreads();
+    }
+    if (pgroup == 0) __syncthreads();
+    return;
+  }
   for (int t = 0; t <= n_tiles; ++t) {
     // The wave in its MFMA cluster gets issue priority over the SIMD's other
     // wave (in its softmax cluster), so the matrix core is fed first.
