@@ -428,6 +428,26 @@ __global__ __launch_bounds__(kNT, 1) void wf_attention_fp8k_kernel(const AttnArg
   if (pgroup == 1) __syncthreads();
   bool staged = false;
   int ptp = 0;                                    // tile-in-page of the softmax's tile
+  // A wave whose 32 query rows all lie past N (the last query tile of a
+  // chunk) has no products to compute: it only stages its share of every
+  // tile and passes the same barriers, so its SIMD partner has the matrix
+  // core to itself.
+  if (__builtin_amdgcn_readfirstlane(qt * BM + wave * 32) >= N) {
+    for (int t = 0; t <= n_tiles; ++t) {
+      __syncthreads();
+      if (t < n_tiles) {
+        if (staged) store_tile((t + 2) & (kStages - 1));
+        staged = false;
+        if (t + 3 < n_tiles) {
+          load_next();
+          staged = true;
+        }
+      }
+      __syncthreads();
+    }
+    if (pgroup == 0) __syncthreads();
+    return;
+  }
   for (int t = 0; t <= n_tiles; ++t) {
     __builtin_amdgcn_s_setprio(1);
     mfma_cluster((t - 1) & (kStages - 1), t & (kStages - 1));
