@@ -117,6 +117,8 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--dit", action="store_true")
     ap.add_argument("--ffn", type=int, default=0, help="DiT FFN width (0: 8960, or 13824 at 40 heads)")
+    ap.add_argument("--split", choices=("auto", "off", "force"), default="auto",
+                    help="attention split mode of the steady-round bench (wf_set_attention_split)")
     return ap.parse_args()
 
 
@@ -219,6 +221,8 @@ def request_bench(args, w):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     sess = Session(w.config(), device=dev)
+    wf.wf_set_attention_split(sess.h, {"auto": wf.WF_SPLIT_AUTO, "off": wf.WF_SPLIT_OFF,
+                                       "force": wf.WF_SPLIT_FORCE}[args.split])
     S, L = w.S, w.n_layers
     n_rounds = w.n_chunk + w.S
     sets = []
@@ -500,6 +504,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     sess = Session(w.config(), device=dev)
+    wf.wf_set_attention_split(sess.h, {"auto": wf.WF_SPLIT_AUTO, "off": wf.WF_SPLIT_OFF,
+                                       "force": wf.WF_SPLIT_FORCE}[args.split])
     S, L = w.S, w.n_layers
     w_store = w.W + w.S if w.W_store < 0 else w.W_store
     k_steady = w.S + max(w.W, w_store) + 1         # full width and full window
@@ -582,7 +588,8 @@ def main():
                    "W_store": w_store, "anchor": w.anchor, "n_chunk": w.n_chunk,
                    "tokens_per_chunk": w.n_tokens, "heads": w.n_heads,
                    "head_dim": w.head_dim, "layers": L,
-                   "rounds_timed": [k0, k0 + args.steps - 1], "n_rounds": n_rounds},
+                   "rounds_timed": [k0, k0 + args.steps - 1], "n_rounds": n_rounds,
+                   "attention_split": args.split},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak,
                      "unit": "TFLOP/s", "frac": achieved / peak,
                      "traffic": measured_traffic(kind, w.name),

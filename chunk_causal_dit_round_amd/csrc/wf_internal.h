@@ -14,6 +14,10 @@
 
 namespace wf {
 struct DitState;  // hipBLASLt handle and product plans, created on first use
+// A split query group: its context runs as pages [0, at) and [at, n).
+struct SplitAt {
+  int stage, at;
+};
 }
 
 struct wf_handle {
@@ -31,7 +35,7 @@ struct wf_handle {
   // device, the mode, and the split chosen per list of group page counts.
   int n_cu = 256;
   int split_mode = WF_SPLIT_AUTO;
-  std::map<std::vector<int>, std::vector<int>> split_cache;
+  std::map<std::vector<int>, std::vector<wf::SplitAt>> split_cache;
 };
 
 namespace wf {

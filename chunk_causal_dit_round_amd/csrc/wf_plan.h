@@ -61,9 +61,9 @@ inline int slot_denoise(const Shape& sh, int64_t k, int j) {
 }
 
 // At most this many query groups of one attention launch are split into two
-// halves over their pages (bf16, FP8 and FP8K rounds); the halves' partial
+// parts over their pages (bf16, FP8 and FP8K rounds); the parts' partial
 // results live in device scratch after the RoPE tables.
-constexpr int kMaxSplit = 2;
+constexpr int kMaxSplit = WF_MAX_SPLIT;
 
 // Bytes of caller buffers.  The table buffer holds the RoPE tables
 // (rope_table_bytes, rounded up to 256) and then the split scratch.  The

@@ -157,10 +157,12 @@ double launch_end(const wf::Shape& sh, int n_cu, int per_group, const std::vecto
   return end;
 }
 
-// Stages of the groups to split (at most kMaxSplit), for the handle's mode.
-std::vector<int> choose_split(wf_handle* h, const wf_plan& p, const std::vector<int>& active) {
+// Groups to split and where, for the handle's mode: under WF_SPLIT_AUTO at
+// most max_split groups (those whose partial results the scratch holds).
+std::vector<wf::SplitAt> choose_split(wf_handle* h, const wf_plan& p, const std::vector<int>& active,
+                                      int max_split) {
   const wf::Shape& sh = h->sh;
-  std::vector<int> none;
+  std::vector<wf::SplitAt> none;
   if (sh.dtype == WF_F32 || h->split_mode == WF_SPLIT_OFF) return none;
   std::vector<int> cand;   // splittable groups, longest first (ties: lower stage)
   for (const int s : active)
@@ -169,9 +171,11 @@ std::vector<int> choose_split(wf_handle* h, const wf_plan& p, const std::vector<
                    [&](int x, int y) { return p.groups[x].n_pages > p.groups[y].n_pages; });
   if (h->split_mode == WF_SPLIT_FORCE) {
     if (cand.size() > size_t(wf::kMaxSplit)) cand.resize(wf::kMaxSplit);
-    return cand;
+    std::vector<wf::SplitAt> halves;
+    for (const int s : cand) halves.push_back({s, p.groups[s].n_pages / 2});
+    return halves;
   }
-  std::vector<int> key;
+  std::vector<int> key{max_split};
   for (const int s : active) key.push_back(p.groups[s].n_pages);
   const auto hit = h->split_cache.find(key);
   if (hit != h->split_cache.end()) return hit->second;
@@ -183,30 +187,36 @@ std::vector<int> choose_split(wf_handle* h, const wf_plan& p, const std::vector<
   // one compute unit at 1.1 PFLOP/s over n_cu units, plus 2 tiles of launch gap.
   const double tile_s = double(bm) * 64.0 * sh.D * 4.0 / (1.1e15 / h->n_cu);
   const double merge = 2.0 + 10.0 * double(sh.N) * sh.H * sh.D / 5e12 / tile_s;
-  auto cost = [&](const std::vector<int>& sp) {
+  auto cost = [&](const std::vector<wf::SplitAt>& sp) {
     std::vector<int> pages;
     for (const int s : active) {
       const int n = p.groups[s].n_pages;
-      if (std::find(sp.begin(), sp.end(), s) == sp.end()) {
+      int at = 0;
+      for (const wf::SplitAt& x : sp)
+        if (x.stage == s) at = x.at;
+      if (at == 0) {
         pages.push_back(n);
       } else {
-        pages.push_back(n / 2);
-        pages.push_back(n - n / 2);
+        pages.push_back(at);
+        pages.push_back(n - at);
       }
     }
     return launch_end(sh, h->n_cu, per_group, pages) + merge * double(sp.size());
   };
-  std::vector<int> best;
+  // Halves of any one group, then of any two; a strictly lower modelled end
+  // is needed to split, or to split more.
+  std::vector<wf::SplitAt> best;
   double best_cost = cost(best);
-  for (size_t i = 0; i < cand.size(); ++i) {
-    const std::vector<int> one{cand[i]};
+  for (size_t i = 0; i < cand.size() && max_split >= 1; ++i) {
+    const std::vector<wf::SplitAt> one{{cand[i], p.groups[cand[i]].n_pages / 2}};
     const double c1 = cost(one);
     if (c1 < best_cost) best_cost = c1, best = one;
   }
-  if (wf::kMaxSplit >= 2) {
+  if (max_split >= 2) {
     for (size_t i = 0; i < cand.size(); ++i)
       for (size_t j = i + 1; j < cand.size(); ++j) {
-        const std::vector<int> two{cand[i], cand[j]};
+        const std::vector<wf::SplitAt> two{{cand[i], p.groups[cand[i]].n_pages / 2},
+                                           {cand[j], p.groups[cand[j]].n_pages / 2}};
         const double c2 = cost(two);
         if (c2 < best_cost) best_cost = c2, best = two;
       }
@@ -239,10 +249,20 @@ wf_status do_attention(wf_handle* h, const wf_plan& p, int layer, const void* q_
   std::vector<int> active;
   for (int s = 0; s <= sh.S; ++s)
     if (p.groups[s].n_pages > 0) active.push_back(s);
-  const std::vector<int> split = choose_split(h, p, active);
+  if (!scratch) {
+    scratch = static_cast<char*>(h->tables) + (wf::rope_table_bytes(sh) + 255) / 256 * 256;
+    scratch_cap = wf::split_scratch_bytes(sh);
+  }
+  // Two parts per split group: O [N][H][D] fp32 of every part, then (e, l)
+  // [N][H] of every part.
+  const size_t nh = size_t(sh.N) * size_t(sh.H);
+  const size_t nhd = nh * size_t(sh.D);
+  const size_t per_split = 2 * (nhd + 2 * nh) * sizeof(float);
+  const int max_split = static_cast<int>(std::min<size_t>(wf::kMaxSplit, scratch_cap / per_split));
+  const std::vector<wf::SplitAt> split = choose_split(h, p, active, max_split);
 
-  // Runs of the launch: whole groups, or the two halves of a split group
-  // (pages [0, n/2) and [n/2, n)), longest first (ties: lower stage first).
+  // Runs of the launch: whole groups, or the two parts of a split group
+  // (pages [0, at) and [at, n)), longest first (ties: lower stage first).
   struct Run {
     int stage, page0, n_pages, part;
   };
@@ -250,13 +270,14 @@ wf_status do_attention(wf_handle* h, const wf_plan& p, int layer, const void* q_
   wf::CombineArgs c{};
   for (const int s : active) {
     const int n = p.groups[s].n_pages;
-    const auto it = std::find(split.begin(), split.end(), s);
-    if (it == split.end()) {
+    int i = 0;
+    while (i < static_cast<int>(split.size()) && split[i].stage != s) ++i;
+    if (i == static_cast<int>(split.size())) {
       runs.push_back({s, 0, n, -1});
     } else {
-      const int i = static_cast<int>(it - split.begin());
-      runs.push_back({s, 0, n / 2, 2 * i});
-      runs.push_back({s, n / 2, n - n / 2, 2 * i + 1});
+      const int at = split[i].at;
+      runs.push_back({s, 0, at, 2 * i});
+      runs.push_back({s, at, n - at, 2 * i + 1});
       c.stage[i] = s;
     }
   }
@@ -275,16 +296,8 @@ wf_status do_attention(wf_handle* h, const wf_plan& p, int layer, const void* q_
   }
   a.n_groups = static_cast<int>(runs.size());
   a.n_items = item;
-  if (!scratch) {
-    scratch = static_cast<char*>(h->tables) + (wf::rope_table_bytes(sh) + 255) / 256 * 256;
-    scratch_cap = wf::split_scratch_bytes(sh);
-  }
-  // Two halves per split group: O [N][H][D] fp32 of every half, then (e, l)
-  // [N][H] of every half.
-  const size_t nh = size_t(sh.N) * size_t(sh.H);
-  const size_t nhd = nh * size_t(sh.D);
   const size_t parts = 2 * split.size();
-  const size_t need = parts * (nhd + 2 * nh) * sizeof(float);
+  const size_t need = split.size() * per_split;
   if (need > scratch_cap) {
     return fail(WF_ESMALL, "the split chosen needs " + std::to_string(need) +
                                " bytes of split scratch, above the " + std::to_string(scratch_cap) +
@@ -475,6 +488,26 @@ wf_status wf_set_attention_split(wf_handle* h, int32_t mode) {
   if (mode != WF_SPLIT_AUTO && mode != WF_SPLIT_OFF && mode != WF_SPLIT_FORCE)
     return fail(WF_EINVAL, "unknown split mode " + std::to_string(mode));
   h->split_mode = mode;
+  return ok();
+}
+
+wf_status wf_attention_split_choice(wf_handle* h, const wf_plan* plan, int32_t* n_split,
+                                    int32_t* stage, int32_t* at) {
+  if (!h || !plan || !n_split || !stage || !at) return fail(WF_EINVAL, "NULL argument");
+  if (plan->config_hash != h->hash) return fail(WF_EORDER, "plan was made for another config");
+  if (!wf::round_in_range(h->sh, plan->k)) return fail(WF_ERANGE, "plan's round outside the request");
+  wf_plan p;
+  wf::build_plan(h->sh, h->hash, plan->k, &p);
+  if (std::memcmp(&p, plan, sizeof(wf_plan)) != 0) return fail(WF_EINVAL, "plan contents were modified");
+  std::vector<int> active;
+  for (int s = 0; s <= h->sh.S; ++s)
+    if (p.groups[s].n_pages > 0) active.push_back(s);
+  const std::vector<wf::SplitAt> split = choose_split(h, p, active, wf::kMaxSplit);
+  *n_split = static_cast<int32_t>(split.size());
+  for (size_t i = 0; i < split.size(); ++i) {
+    stage[i] = split[i].stage;
+    at[i] = split[i].at;
+  }
   return ok();
 }
 

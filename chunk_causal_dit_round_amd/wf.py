@@ -103,6 +103,8 @@ def _load():
         "wf_wave_attention": (i32, [H, ctypes.POINTER(wf_plan), i32, cvp, vp, vp]),
         "wf_wave_attention_noalloc": (i32, [H, ctypes.POINTER(wf_plan), i32, cvp, vp, vp]),
         "wf_set_attention_split": (i32, [H, i32]),
+        "wf_attention_split_choice": (i32, [H, ctypes.POINTER(wf_plan), ctypes.POINTER(i32),
+                                            ctypes.POINTER(i32), ctypes.POINTER(i32)]),
         "wf_round_commit": (i32, [H, ctypes.POINTER(wf_plan)]),
         "wf_round": (i32, [H, ctypes.POINTER(wf_plan), cvp, cvp, cvp, vp, vp, vp]),
         "wf_dit_workspace_bytes": (i32, [H, ctypes.POINTER(wf_dit_config), ctypes.POINTER(sz)]),
@@ -235,6 +237,19 @@ WF_STATIC_SCRATCH_BYTES = 128 << 20
 
 def wf_set_attention_split(h, mode):
     _check(_lib.wf_set_attention_split(h, mode))
+
+
+WF_MAX_SPLIT = 2
+
+
+def wf_attention_split_choice(h, plan):
+    """[(stage, at), ...]: the groups wf_wave_attention splits for `plan`
+    (pages [0, at) and [at, n) of the group's context)."""
+    n = i32()
+    stage = (i32 * WF_MAX_SPLIT)()
+    at = (i32 * WF_MAX_SPLIT)()
+    _check(_lib.wf_attention_split_choice(h, ctypes.byref(plan), ctypes.byref(n), stage, at))
+    return [(stage[i], at[i]) for i in range(n.value)]
 
 
 def wf_round_commit(h, plan):

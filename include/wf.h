@@ -101,6 +101,7 @@ extern "C" {
 #define WF_MAX_STAGES 8                     /* S <= 8 denoising stages     */
 #define WF_MAX_GROUPS (WF_MAX_STAGES + 1)   /* + the store                 */
 #define WF_MAX_PAGES 48                     /* key pages per query group   */
+#define WF_MAX_SPLIT 2                      /* split query groups per launch */
 
 typedef enum {
   WF_OK = 0,
@@ -340,10 +341,13 @@ wf_status wf_wave_attention(wf_handle* h, const wf_plan* plan, int32_t layer,
  * with that device current).  Every call on one GPU, from any handle,
  * shares that GPU's one array and leaves its partial results there, so two
  * such calls in flight at once on one GPU (different streams, handles or
- * threads) race: order them.  WF_ESMALL, before any launch, when the split
- * the handle's mode chooses needs more than WF_STATIC_SCRATCH_BYTES
- * (2 (N H D + 2 N H) * 4 bytes per split group); WF_SPLIT_OFF needs none.
- * WF_EDEVICE if the array's address cannot be found. */
+ * threads) race: order them.  Split groups need 2 (N H D + 2 N H) * 4
+ * bytes each: under WF_SPLIT_AUTO the choice is made among the splits whose
+ * partial results fit the array (none at the 14B class), so it can differ
+ * from wf_wave_attention's; WF_ESMALL, before any launch, when a forced
+ * split (WF_SPLIT_FORCE) needs more than WF_STATIC_SCRATCH_BYTES.
+ * WF_SPLIT_OFF needs none.  WF_EDEVICE if the array's address cannot be
+ * found. */
 wf_status wf_wave_attention_noalloc(wf_handle* h, const wf_plan* plan, int32_t layer,
                                     const void* d_q_rot, void* d_out, void* stream);
 
@@ -357,11 +361,26 @@ wf_status wf_wave_attention_noalloc(wf_handle* h, const wf_plan* plan, int32_t l
  * launch merges the two softmax partials exactly (WF §4.2 gives the per-
  * stage key counts that make the groups' lengths unequal).  WF_SPLIT_AUTO
  * (the default) models the launch as work-groups taken longest first by
- * the device's compute units and splits the at most two groups that
- * minimise that model's end time plus the merge; the choice is cached per
- * list of group lengths.  Results of the modes agree up to rounding.
+ * the device's compute units and splits the at most WF_MAX_SPLIT groups
+ * that minimise that model's end time plus the merge; the choice is cached
+ * per list of group lengths.  WF_SPLIT_FORCE splits the two longest groups
+ * (>= 2 pages).  Results of the modes agree up to rounding.
  * WF_EINVAL for a NULL handle or an unknown mode.  Host only. */
 wf_status wf_set_attention_split(wf_handle* h, int32_t mode);
+
+/* The split wf_wave_attention makes for `plan` under the handle's split
+ * mode (see wf_set_attention_split; wf_wave_attention_noalloc chooses among
+ * the splits its static array holds): *n_split groups (0..WF_MAX_SPLIT);
+ * group i is query stage stage[i], run as pages [0, at[i]) and
+ * [at[i], n) of its context (at[i] = n/2).  stage and at have room for
+ * WF_MAX_SPLIT entries; entries past *n_split are left untouched.  The
+ * model uses the compute-unit count of the device current at wf_bind (256
+ * before).
+ * WF_EINVAL for a NULL argument or a modified plan; WF_EORDER for a plan
+ * of another config; WF_ERANGE for a round outside the request.  Host only
+ * (needs no bound pool). */
+wf_status wf_attention_split_choice(wf_handle* h, const wf_plan* plan, int32_t* n_split,
+                                    int32_t* stage, int32_t* at);
 
 /* End the round (WF App. B.3): requires every layer published; advances
  * the expected round.  Host only: the store page is promoted in place. */

@@ -32,7 +32,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 21, names
+    assert len(names) == 22, names
     assert {"wf_dit_workspace_bytes", "wf_dit_layer", "wf_dit_round"} <= set(names)
     lib = ctypes.CDLL(wf.LIB_PATH)
     for n in names:
@@ -405,3 +405,127 @@ def test_device_failure_is_reported_as_wf_edevice():
         assert wf.status_of(wf.wf_kv_publish, h, plan, 0, fake, fake, fake, fake, 0) == wf.WF_EINVAL
     finally:
         wf.wf_destroy(h)
+
+
+# ---- the attention launch's split choice (host only) ----
+
+def _model_split(w, pages_by_stage, n_cu=256):
+    """The split model wf_set_attention_split documents, written out: every
+    work-group (group or half, head, 256 query rows) taken longest first by
+    n_cu compute units, one at a time each; a work-group costs its key
+    tiles + 2; plus the merge per split group.  Returns the strictly
+    cheapest split found scanning none, the halves of every single group,
+    then of every pair."""
+    import heapq
+    import math
+
+    N, H, D = w.Hh * w.Ww * w.F, w.n_heads, w.head_dim
+    bm = 256
+    per_group = H * ((N + bm - 1) // bm)
+    T = (N + 63) // 64
+
+    def end(pages):
+        free_at = [0.0] * n_cu
+        e = 0.0
+        for p in sorted(pages, reverse=True):
+            tiles = (math.ceil(p * N / 64.0) if w.dtype == wf.WF_BF16 else float(p * T)) + 2.0
+            for _ in range(per_group):
+                t = heapq.heappop(free_at) + tiles
+                heapq.heappush(free_at, t)
+                e = max(e, t)
+        return e
+
+    tile_s = bm * 64.0 * D * 4.0 / (1.1e15 / n_cu)
+    merge = 2.0 + 10.0 * N * H * D / 5e12 / tile_s
+    active = [s for s in sorted(pages_by_stage) if pages_by_stage[s] > 0]
+
+    def cost(sp):
+        pages = []
+        for s in active:
+            n = pages_by_stage[s]
+            pages += [n // 2, n - n // 2] if s in sp else [n]
+        return end(pages) + merge * len(sp)
+
+    cand = sorted([s for s in active if pages_by_stage[s] >= 2], key=lambda s: -pages_by_stage[s])
+    best, best_cost = [], cost([])
+    for s in cand:
+        c = cost([s])
+        if c < best_cost:
+            best, best_cost = [s], c
+    for i in range(len(cand)):
+        for j in range(i + 1, len(cand)):
+            c = cost([cand[i], cand[j]])
+            if c < best_cost:
+                best, best_cost = [cand[i], cand[j]], c
+    return [(s, pages_by_stage[s] // 2) for s in best]
+
+
+def _group_pages(p):
+    return {s: p.groups[s].n_pages for s in range(p.S + 1)}
+
+
+@pytest.mark.parametrize("w", [WAN13B_4STEP, WAN13B_4STEP_FP8, WAN13B_4STEP_FP8K],
+                         ids=lambda w: w.name)
+def test_split_choice_follows_the_launch_model(w):
+    """AUTO's choice equals the documented model's on every distinct list of
+    group lengths of the whole 1.3B request (fill, steady, drain); every
+    split is of an active group, in halves; repeated queries agree."""
+    h = wf.wf_create(w.config())
+    try:
+        seen = {}
+        for k in range(w.n_chunk + w.S):
+            p = wf.wf_round_plan(h, k)
+            pages = _group_pages(p)
+            key = tuple(pages[s] for s in sorted(pages))
+            got = wf.wf_attention_split_choice(h, p)
+            assert got == wf.wf_attention_split_choice(h, p)
+            assert len(got) <= wf.WF_MAX_SPLIT and len({s for s, _ in got}) == len(got)
+            for s, at in got:
+                assert pages[s] >= 2 and at == pages[s] // 2
+            if key not in seen:
+                seen[key] = _model_split(w, pages)
+            assert got == seen[key], (k, pages)
+        steady = wf.wf_round_plan(h, 16)
+        assert [steady.groups[s].n_pages for s in range(5)] == [10, 9, 8, 7, 10]
+        # the steady round's choice: the 7-page group, as 3 + 4 pages
+        assert wf.wf_attention_split_choice(h, steady) == [(3, 3)]
+    finally:
+        wf.wf_destroy(h)
+
+
+def test_split_choice_off_force_and_fp32():
+    h = wf.wf_create(WAN13B_4STEP.config())
+    try:
+        p = wf.wf_round_plan(h, 16)
+        wf.wf_set_attention_split(h, wf.WF_SPLIT_OFF)
+        assert wf.wf_attention_split_choice(h, p) == []
+        wf.wf_set_attention_split(h, wf.WF_SPLIT_FORCE)
+        # the two longest groups (10 pages: stage 0 and the store), halves
+        assert wf.wf_attention_split_choice(h, p) == [(0, 5), (4, 5)]
+        wf.wf_set_attention_split(h, wf.WF_SPLIT_AUTO)
+        assert wf.wf_attention_split_choice(h, p) == [(3, 3)]
+    finally:
+        wf.wf_destroy(h)
+    h = wf.wf_create(TINY_FP32.config())
+    try:
+        wf.wf_set_attention_split(h, wf.WF_SPLIT_FORCE)
+        for k in range(TINY_FP32.n_chunk + TINY_FP32.S):
+            assert wf.wf_attention_split_choice(h, wf.wf_round_plan(h, k)) == []
+    finally:
+        wf.wf_destroy(h)
+
+
+def test_split_choice_errors():
+    h = wf.wf_create(WAN13B_4STEP.config())
+    other = wf.wf_create(TINY_FP32.config())
+    try:
+        p = wf.wf_round_plan(h, 16)
+        assert wf.status_of(wf.wf_attention_split_choice, None, p) == wf.WF_EINVAL
+        assert wf.status_of(wf.wf_attention_split_choice, other, p) == wf.WF_EORDER
+        bad = wf.wf_round_plan(h, 16)
+        bad.groups[1].n_pages += 1
+        assert wf.status_of(wf.wf_attention_split_choice, h, bad) == wf.WF_EINVAL
+        assert "modified" in wf.wf_last_error()
+    finally:
+        wf.wf_destroy(h)
+        wf.wf_destroy(other)
