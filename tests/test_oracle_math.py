@@ -137,9 +137,11 @@ def test_round_reduces_to_causal_sdpa():
     raw = Raw(c, seed=11, scale=2.0)
     k = 7
     res = WR.round_outputs(c, k, 0, raw)
-    # chunk order: store chunk k-S first, then k-S+1 ... k (stage S .. 0)
+    # chunk order: store chunk k-S first, then k-S+1 ... k (stage S .. 0);
+    # queries and keys of chunk k-s both at that chunk's own frame (R10)
     stages = list(range(S, -1, -1))
-    q = np.concatenate([res[s][0] for s in stages])                 # [S+1, H, d]
+    q = np.concatenate([R.rope3d(raw(k, 0, s, "q"), k - s, 1, 1, 1) for s in stages])
+    np.testing.assert_array_equal(np.concatenate([res[s][0] for s in stages]), q)
     kk = np.concatenate([R.rope3d(raw(k, 0, s, "k"), k - s, 1, 1, 1) for s in stages])
     vv = np.concatenate([raw(k, 0, s, "v") for s in stages])
     t = lambda a: torch.from_numpy(a.transpose(1, 0, 2).copy())
@@ -158,7 +160,8 @@ def test_rolling_mask_reduces_to_dense_sdpa():
     k = 9
     for s in range(c.S):
         got = WR.group_output(c, k, s, 0, raw)
-        q = WR.q_rot(c, k, s, 0, raw)
+        # the denoiser's queries at its chunk's own frames (R10)
+        q = R.rope3d(raw(k, 0, s, "q"), c.F * (k - s), c.F, c.Hh, c.Ww)
         kk, vv = WR.group_keys(c, k, s, 0, raw)
         assert kk.shape[0] == c.n_c * (1 + 2 + 1 + 3)
         t = lambda a: torch.from_numpy(a.transpose(1, 0, 2).copy())

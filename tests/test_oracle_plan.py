@@ -261,6 +261,62 @@ def _simulate_slots(c, rounds):
         prev_reads = reads
 
 
+@pytest.mark.parametrize("c", [cfg(S=4, W=4, n_chunk=40), cfg(S=2, W=2, W_store=4, n_chunk=16),
+                               cfg(S=3, W=0, anchor=0, n_chunk=12), cfg(S=1, W=5, W_store=2, n_chunk=25),
+                               cfg(S=3, W=3, W_store=1, n_chunk=20)],
+                         ids=lambda c: f"S{c.S}W{c.W}/{c.W_store}A{c.anchor}N{c.n_chunk}")
+def test_evicted_chunk_is_the_oldest_retained_page(c):
+    """Brute force of the clean list (App. B.3, B.8): after each round the
+    store's chunk joins the retained list (the anchor chunk 0 never does, R4)
+    and, past max(W, W_store) pages, the oldest leaves; that one is the
+    round's evicted chunk, and every history page a later round reads is
+    still retained."""
+    retained = []
+    for k in range(c.n_rounds):
+        p = P.plan(c, k)
+        for g in p["groups"]:
+            for kd, ch, _ in g["entries"]:
+                if kd == P.HISTORY:
+                    assert ch in retained
+        dropped = -1
+        if p["cells"][c.S]["active"]:
+            ch = k - c.S
+            if not (c.anchor == 1 and ch == 0):
+                retained.append(ch)
+            if len(retained) > c.w_max:
+                dropped = retained.pop(0)
+        assert p["evict"] == dropped, (k, p["evict"], dropped)
+
+
+@pytest.mark.parametrize("c", [cfg(S=3, W=2, n_chunk=9, F=1, Hh=2, Ww=3, heads=2, d=16, L=2),
+                               cfg(S=2, W=1, W_store=3, anchor=0, n_chunk=6, F=2, Hh=1, Ww=3,
+                                   heads=3, d=8, L=1, mask=P.MASK_ROLLING)],
+                         ids=["wave", "rolling"])
+def test_plan_flops_match_torch_flop_counter(c):
+    """The plan's FLOPs (what the roofline divides by) equal what torch's FLOP
+    counter reports for the two products of plain attention (scores Q K^T,
+    then P V) of every active group over its context, every layer, in every
+    round.  (The counter does not see torch's CPU scaled_dot_product_attention
+    kernel, so the products are run as matmuls.)"""
+    import torch
+    from torch.utils.flop_counter import FlopCounterMode
+
+    for k in range(c.n_rounds):
+        p = P.plan(c, k)
+        counter = FlopCounterMode(display=False)
+        with counter:
+            for _ in range(c.n_layers):
+                for g in p["groups"]:
+                    n_k = len(g["entries"]) * c.n_c
+                    if n_k == 0:
+                        continue
+                    q = torch.zeros(1, c.n_heads, c.n_c, c.head_dim, dtype=torch.float64)
+                    kv = torch.zeros(1, c.n_heads, n_k, c.head_dim, dtype=torch.float64)
+                    q @ kv.transpose(-1, -2)                         # scores
+                    torch.zeros(1, c.n_heads, c.n_c, n_k, dtype=torch.float64) @ kv   # P V
+        assert p["flops"] == counter.get_total_flops(), k
+
+
 def test_payload_bytes_formula():
     # Per-chunk K+V page size equals the page's per-edge payload formula.
     c = cfg(S=4, W=4, n_chunk=133, F=3, Hh=30, Ww=52, heads=12, d=128)
